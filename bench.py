@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""FP32 GEMM benchmark on one MI355X: TFLOP/s and fraction of the roofline.
+
+One step is one C = A x B through the C ABI (libtra_gemm.so) on device-
+resident inputs.  The headline workload is M = N = K = 1024 with seeded
+uniform[-1, 1) inputs (50 timed launches after warm-up, as the page "GEMM
+kernel test code & optimization (1024^3 experiment)" times its kernels);
+M = N = K = 4096 with normal(0, 1) inputs is reported beside it as
+"secondary".  Every rung of the kernel ladder is also timed on both shapes
+("ladder").
+
+Timing: HIP events recorded on the stream the kernels are launched on
+(torch's current stream), around `--steps` back-to-back launches, after
+`--warmup` launches; per-launch event pairs give min/median.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP32 GEMM TFLOP/s and % of roofline at 1024³ and 4096³, 1× MI355X"
+PRIMARY = "uniform1024"
+SECONDARY = "normal4096"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    """sha256 of the HIP sources of the MFMA rung (identifies the kernel build
+    that a stored counter reading belongs to)."""
+    h = hashlib.sha256()
+    for f in ("gemm_mfma.hip", "gemm_internal.h"):
+        with open(os.path.join(ROOT, "tiling_roofline_analysis_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary for
+    this workload, if it was taken on the current kernel sources, else None."""
+    path = os.path.join(PROFILES, f"traffic_gemm_mfma_f32_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_variant(tra, torch, variant, w, dA, dB, dC, steps, warmup):
+    stream = torch.cuda.current_stream()
+    handle = stream.cuda_stream
+    pa, pb, pc = dA.data_ptr(), dB.data_ptr(), dC.data_ptr()
+    M, N, K = w.M, w.N, w.K
+    fn = tra.load().gemm_f32_variant
+
+    def launch():
+        st = fn(variant, M, N, K, pa, K, pb, N, pc, N, handle)
+        if st != tra.TRA_OK:
+            raise tra.TraError(st, "gemm_f32_variant")
+
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        launch()
+    end.record(stream)
+    end.synchronize()
+    avg_ms = start.elapsed_time(end) / steps
+    # per-launch pairs (a separate pass, so the loop above has no extra events)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(min(steps, 50))]
+    for s, e in pairs:
+        s.record(stream)
+        launch()
+        e.record(stream)
+    torch.cuda.synchronize()
+    per = [s.elapsed_time(e) for s, e in pairs]
+    return avg_ms, min(per), statistics.median(per)
+
+
+def cpu_baseline(w):
+    """The CPU oracle on the full headline product, on the host's cores."""
+    import oracle
+    A, B = w.make()
+    threads = oracle.default_threads()
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.gemm(A, B, nthreads=threads)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {
+        "value": w.flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": (f"full {w.M}x{w.N}x{w.K} product ({w.what}), binary64 triple loop, "
+                   f"median of 3 runs = {t:.3f} s"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ladder", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this GEMM has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tiling_roofline_analysis_amd as tra
+    from tiling_roofline_analysis_amd import inputs
+    from tiling_roofline_analysis_amd import roofline as rl
+
+    if not os.path.exists(tra.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    tra.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    def measure(name, steps, warmup, ladder):
+        w = inputs.WORKLOADS[name]
+        A, B = w.make()
+        dA = torch.from_numpy(A).to("cuda:0")
+        dB = torch.from_numpy(B).to("cuda:0")
+        dC = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda:0")
+        log(f"[{name}] {tra.tra_gemm_describe(tra.AUTO, w.M, w.N, w.K)}")
+        avg, mn, med = time_variant(tra, torch, tra.AUTO, w, dA, dB, dC, steps, warmup)
+        rep = rl.gemm_roofline(w.M, w.N, w.K, avg * 1e-3)
+        log(f"[{name}] auto(mfma): {avg * 1e3:.2f} us/launch (min {mn * 1e3:.2f}, "
+            f"median {med * 1e3:.2f}) = {rep['tflops']:.2f} TFLOP/s, "
+            f"{100 * rep['frac_of_roof']:.1f}% of roof")
+        out = {"w": w, "avg_ms": avg, "min_ms": mn, "median_ms": med, "rep": rep, "ladder": {}}
+        if ladder:
+            for v in tra.LADDER:
+                # keep each rung's timed region to about half a second
+                probe, _, _ = time_variant(tra, torch, v, w, dA, dB, dC, 1, 1)
+                st = max(3, min(steps, int(500.0 / max(probe, 1e-3))))
+                a2, m2, md2 = time_variant(tra, torch, v, w, dA, dB, dC, st, 1)
+                r2 = rl.gemm_roofline(w.M, w.N, w.K, a2 * 1e-3)
+                name_v = tra.tra_gemm_variant_name(v)
+                peak = rl.PEAK_FP32_MFMA_TFLOPS if v == tra.MFMA else rl.PEAK_FP32_VALU_TFLOPS
+                out["ladder"][name_v] = {
+                    "ms": round(a2, 5), "tflops": round(r2["tflops"], 3),
+                    "frac_of_fp32_peak": round(r2["tflops"] / rl.PEAK_FP32_MFMA_TFLOPS, 4),
+                    "frac_of_unit_peak": round(r2["tflops"] / peak, 4), "steps": st}
+                log(f"[{name}] {name_v:12s} {a2 * 1e3:10.2f} us  {r2['tflops']:8.2f} TFLOP/s")
+        del dA, dB, dC
+        torch.cuda.empty_cache()
+        return out
+
+    t_wall = time.perf_counter()
+    prim = measure(PRIMARY, args.steps, args.warmup, not args.no_ladder)
+    sec = None if args.no_secondary else measure(SECONDARY, args.steps, args.warmup,
+                                                 not args.no_ladder)
+    gpu_wall = time.perf_counter() - t_wall
+
+    def roofline_obj(m, workload):
+        rep = m["rep"]
+        return {"bound": "mfma", "achieved": round(rep["tflops"], 3),
+                "peak": rl.PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(rep["tflops"] / rl.PEAK_FP32_MFMA_TFLOPS, 4),
+                "traffic": stored_traffic(workload)}
+
+    w = prim["w"]
+    line = {
+        "metric": METRIC,
+        "value": round(prim["rep"]["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(prim["avg_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"FP32 GEMM M=N=K={w.M} row-major, {w.what}",
+                   "M": w.M, "N": w.N, "K": w.K, "kernel": tra.tra_gemm_describe(tra.AUTO, w.M, w.N, w.K)},
+        "roofline": roofline_obj(prim, PRIMARY),
+        "detail": {
+            "min_ms": round(prim["min_ms"], 5), "median_ms": round(prim["median_ms"], 5),
+            "ai_flop_per_byte": round(prim["rep"]["ai"], 2),
+            "algorithmic_bytes": prim["rep"]["bytes"],
+            "source_digest": source_digest(), "gpu_wall_s": round(gpu_wall, 2),
+            "device": torch.cuda.get_device_name(0),
+        },
+    }
+    if prim["ladder"]:
+        line["ladder"] = {PRIMARY: prim["ladder"]}
+    if sec is not None:
+        ws = sec["w"]
+        line["secondary"] = {
+            "workload": f"FP32 GEMM M=N=K={ws.M} row-major, {ws.what}",
+            "value": round(sec["rep"]["tflops"], 3), "unit": "TFLOP/s",
+            "ms_per_step": round(sec["avg_ms"], 5), "min_ms": round(sec["min_ms"], 5),
+            "kernel": tra.tra_gemm_describe(tra.AUTO, ws.M, ws.N, ws.K),
+            "roofline": roofline_obj(sec, SECONDARY),
+        }
+        if sec["ladder"]:
+            line.setdefault("ladder", {})[SECONDARY] = sec["ladder"]
+    if not args.no_cpu_baseline:
+        log("[cpu_baseline] timing the oracle ...")
+        line["cpu_baseline"] = cpu_baseline(inputs.WORKLOADS[PRIMARY])
+        log(f"[cpu_baseline] {line['cpu_baseline']['value'] * 1e3:.3f} GFLOP/s")
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,151 @@
+/*
+ * tra_gemm.h -- C ABI of the MI355X (gfx950) single-precision GEMM library
+ * libtra_gemm.so.
+ *
+ * The operation is C = A x B on row-major binary32 matrices:
+ *
+ *     C[i*ldc + j] := sum over k < K of A[i*lda + k] * B[k*ldb + j]
+ *                     for 0 <= i < M, 0 <= j < N.
+ *
+ * Definition: page "GEMM kernel test code & optimization (1024^3 experiment)"
+ * (teach-meaning.tistory.com/1513), section "Mathematical definition" (one
+ * k-sum per element of C, 2*M*N*K flops) and section "Memory layout"
+ * (row-major: A[row*K + k], B[k*N + col], C[row*N + col]; here the leading
+ * dimensions lda, ldb, ldc generalise K, N, N).  The result overwrites C:
+ * the accumulator starts at zero and is stored once, as in both kernels of
+ * that page (sections "How the naive GEMM kernel works" and "Shared-memory
+ * tiled GEMM").  Elements of C outside the first N columns of each row are
+ * never touched.
+ *
+ * Ownership and memory: A, B and C are device pointers owned by the caller
+ * (for example torch tensors on the current HIP device).  No entry point
+ * allocates, frees or copies host memory; all work is enqueued on `stream`.
+ *
+ * Asynchrony: gemm_f32 and gemm_f32_variant return once the kernels are
+ * enqueued on `stream` (a hipStream_t; NULL means the null stream of the
+ * current device).  Synchronise the stream before reading C on the host.
+ *
+ * Errors: every entry point returns a tra_status and never throws.  The
+ * argument checks run on the host before anything is enqueued; a rejected
+ * call leaves C untouched.  A launch failure returns TRA_ERR_HIP and keeps
+ * the hipError_t for tra_last_hip_error() (per calling thread).
+ *
+ * Numerics: products and sums are binary32 with round-to-nearest-even.  The
+ * order of the k-sum depends on the variant and tile shape, so results on
+ * general inputs may differ between variants in the last bits; inputs whose
+ * partial sums are all exactly representable (e.g. small integers) give
+ * identical bits in every variant.
+ */
+#ifndef TRA_GEMM_H
+#define TRA_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Symbols of the ABI are the only ones the library exports. */
+#define TRA_API __attribute__((visibility("default")))
+
+typedef enum tra_status {
+    TRA_OK = 0,
+    TRA_ERR_INVALID_ARG = 1,   /* a size, stride, pointer or variant is invalid */
+    TRA_ERR_UNSUPPORTED = 2,   /* valid but beyond this library (e.g. grid too large) */
+    TRA_ERR_HIP = 3            /* the HIP runtime reported an error */
+} tra_status;
+
+/*
+ * The kernel ladder.  Each rung is a hand-written gfx950 kernel and each
+ * handles shapes that are not tile multiples by zero-filling the staged
+ * tiles and masking the stores.
+ *   NAIVE        one lane per element of C, K-loop straight from global
+ *                memory (page "GEMM kernel test code & optimization
+ *                (1024^3 experiment)", section "How the naive GEMM kernel
+ *                works").
+ *   LDS_TILED    32x32 tiles of A and B staged in LDS, each lane one element
+ *                of C, zero-filled outside the matrices (same page, section
+ *                "Shared-memory tiled GEMM"; page "[AutoMine++] #2 matmul
+ *                trial and error", section "Breaking the memory bottleneck:
+ *                Tiling").
+ *   REGBLOCK_DB  128x128 block tile, 8x8 register micro-tile per lane,
+ *                double-buffered LDS with register prefetch (VALU FMA).
+ *   MFMA         CDNA matrix-core kernel on binary32 inputs
+ *                (v_mfma_f32_32x32x2_f32), double-buffered LDS, tile shape
+ *                chosen from the problem shape.
+ *   AUTO         the library's choice for the shape (currently MFMA).
+ */
+typedef enum tra_gemm_variant {
+    TRA_GEMM_AUTO = 0,
+    TRA_GEMM_NAIVE = 1,
+    TRA_GEMM_LDS_TILED = 2,
+    TRA_GEMM_REGBLOCK_DB = 3,
+    TRA_GEMM_MFMA = 4
+} tra_gemm_variant;
+
+#define TRA_GEMM_VARIANT_COUNT 5
+
+/*
+ * gemm_f32: C = A x B with the library's choice of kernel (TRA_GEMM_AUTO).
+ *
+ *   M, N, K  sizes; M, N, K >= 0.  M == 0 or N == 0 is a no-op (TRA_OK,
+ *            pointers unused).  K == 0 writes C := 0.
+ *   A        device pointer to M rows of lda floats, row-major (may be NULL
+ *            when K == 0); lda >= K.
+ *   B        device pointer to K rows of ldb floats, row-major (may be NULL
+ *            when K == 0); ldb >= N.
+ *   C        device pointer to M rows of ldc floats, row-major; ldc >= N;
+ *            overwritten.  C must not overlap A or B.
+ *   stream   hipStream_t on the current device, or NULL.
+ *
+ * Pointers need only 4-byte alignment; 16-byte aligned bases with
+ * leading dimensions divisible by 4 take the vector-load path.
+ *
+ * Returns TRA_OK, TRA_ERR_INVALID_ARG (negative size, ld too small, NULL
+ * pointer where data is needed, C overlapping A or B), TRA_ERR_UNSUPPORTED
+ * (the launch grid would exceed 2^31 - 1 workgroups) or TRA_ERR_HIP.
+ */
+TRA_API tra_status gemm_f32(int64_t M, int64_t N, int64_t K,
+                    const float *A, int64_t lda,
+                    const float *B, int64_t ldb,
+                    float *C, int64_t ldc,
+                    void *stream);
+
+/*
+ * gemm_f32_variant: as gemm_f32 but runs the given rung of the ladder
+ * (a tra_gemm_variant value).  An unknown variant is TRA_ERR_INVALID_ARG.
+ */
+TRA_API tra_status gemm_f32_variant(int variant,
+                            int64_t M, int64_t N, int64_t K,
+                            const float *A, int64_t lda,
+                            const float *B, int64_t ldb,
+                            float *C, int64_t ldc,
+                            void *stream);
+
+/*
+ * tra_gemm_describe: writes a one-line, NUL-terminated description of the
+ * launch that gemm_f32_variant(variant, M, N, K, ...) would make for
+ * 16-byte-aligned operands with lda = K, ldb = N, ldc = N (kernel name, tile
+ * shape, grid and block size) into buf[0 .. len-1].  Host-only; touches no
+ * device.  Returns TRA_OK, or TRA_ERR_INVALID_ARG for an unknown variant,
+ * negative sizes, or buf == NULL with len > 0.
+ */
+TRA_API tra_status tra_gemm_describe(int variant, int64_t M, int64_t N, int64_t K,
+                             char *buf, size_t len);
+
+/* Static strings for a status or variant value ("unknown" otherwise). */
+TRA_API const char *tra_status_string(int status);
+TRA_API const char *tra_gemm_variant_name(int variant);
+
+/*
+ * The hipError_t of the last call on this thread that returned TRA_ERR_HIP
+ * (0 if none).  Not cleared by later successful calls.
+ */
+TRA_API int tra_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRA_GEMM_H */

@@ -1,0 +1,122 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and its host-side argument checks reject bad calls before anything
+is enqueued (these calls never reach the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiling_roofline_analysis_amd as tra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tra_gemm.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return re.findall(r"TRA_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tra.load()
+
+
+def test_header_declares_the_abi():
+    names = header_functions()
+    assert set(names) == set(tra.ABI_FUNCTIONS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_only_abi_symbols_are_exported():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", tra.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    ours = {s for s in syms if not s.startswith("_")}
+    assert ours == set(tra.ABI_FUNCTIONS), ours
+
+
+def test_status_and_variant_names():
+    assert tra.tra_status_string(tra.TRA_OK) == "ok"
+    assert tra.tra_status_string(tra.TRA_ERR_INVALID_ARG) == "invalid argument"
+    assert tra.tra_status_string(99) == "unknown"
+    for name, v in tra.VARIANTS.items():
+        assert tra.tra_gemm_variant_name(v) == name
+    assert tra.tra_gemm_variant_name(-1) == "unknown"
+
+
+def test_describe_plans():
+    d = tra.tra_gemm_describe(tra.MFMA, 4096, 4096, 4096)
+    assert "gemm_mfma_f32" in d and "tile=256x128x16" in d and "grid=512" in d
+    d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 1024)
+    assert "tile=64x64x32" in d and "grid=256" in d
+    d = tra.tra_gemm_describe(tra.NAIVE, 1024, 1024, 1024)
+    assert "gemm_naive_f32" in d and "grid=4096" in d and "block=256" in d
+    d = tra.tra_gemm_describe(tra.LDS_TILED, 1024, 1024, 1024)
+    assert "tile=32x32x32" in d and "block=1024" in d
+    d = tra.tra_gemm_describe(tra.REGBLOCK_DB, 3000, 2049, 1531)
+    assert "grid=408" in d   # 24 x 17 tiles of 128 x 128
+    assert tra.tra_gemm_describe(tra.AUTO, 16, 16, 16).startswith("variant=auto")
+    with pytest.raises(tra.TraError):
+        tra.tra_gemm_describe(7, 1, 1, 1)
+    with pytest.raises(tra.TraError):
+        tra.tra_gemm_describe(tra.MFMA, -1, 1, 1)
+
+
+# Fake, never-dereferenced device addresses: the checks reject these calls on
+# the host, before any HIP call.
+A_ADDR, B_ADDR, C_ADDR = 0x10000000, 0x20000000, 0x30000000
+INVALID = [
+    # (variant, M, N, K, A, lda, B, ldb, C, ldc)
+    (tra.MFMA, -1, 4, 4, A_ADDR, 4, B_ADDR, 4, C_ADDR, 4),          # negative M
+    (tra.MFMA, 4, -1, 4, A_ADDR, 4, B_ADDR, 4, C_ADDR, 4),          # negative N
+    (tra.MFMA, 4, 4, -1, A_ADDR, 4, B_ADDR, 4, C_ADDR, 4),          # negative K
+    (tra.MFMA, 4, 4, 4, None, 4, B_ADDR, 4, C_ADDR, 4),             # A NULL
+    (tra.MFMA, 4, 4, 4, A_ADDR, 4, None, 4, C_ADDR, 4),             # B NULL
+    (tra.MFMA, 4, 4, 4, A_ADDR, 4, B_ADDR, 4, None, 4),             # C NULL
+    (tra.MFMA, 4, 4, 8, A_ADDR, 7, B_ADDR, 4, C_ADDR, 4),           # lda < K
+    (tra.MFMA, 4, 8, 4, A_ADDR, 4, B_ADDR, 7, C_ADDR, 8),           # ldb < N
+    (tra.MFMA, 4, 8, 4, A_ADDR, 4, B_ADDR, 8, C_ADDR, 7),           # ldc < N
+    (tra.MFMA, 4, 4, 4, A_ADDR, 4, B_ADDR, 4, A_ADDR + 16, 4),      # C overlaps A
+    (tra.MFMA, 4, 4, 4, A_ADDR, 4, B_ADDR, 4, B_ADDR + 60, 4),      # C overlaps B's last word
+    (tra.NAIVE, 4, 4, 4, A_ADDR, 4, B_ADDR, 4, B_ADDR - 4, 4),      # C's last word on B's first
+    (5, 4, 4, 4, A_ADDR, 4, B_ADDR, 4, C_ADDR, 4),                  # unknown variant
+    (-1, 4, 4, 4, A_ADDR, 4, B_ADDR, 4, C_ADDR, 4),                 # unknown variant
+    (tra.MFMA, 1 << 40, 4, 4, A_ADDR, 1 << 40, B_ADDR, 4, C_ADDR, 4),   # extent overflow
+]
+
+
+@pytest.mark.parametrize("args", INVALID)
+def test_invalid_arguments_rejected_on_host(args):
+    v, M, N, K, A, lda, B, ldb, C, ldc = args
+    st = tra.gemm_f32_variant(v, M, N, K, A, lda, B, ldb, C, ldc, None)
+    assert st == tra.TRA_ERR_INVALID_ARG
+
+
+def test_gemm_f32_checks_too():
+    assert tra.gemm_f32(4, 4, 4, None, 4, B_ADDR, 4, C_ADDR, 4, None) == tra.TRA_ERR_INVALID_ARG
+
+
+def test_grid_too_large_is_unsupported():
+    # 2^36 rows x 64 columns of C with the naive rung needs 2^34 workgroups
+    M = 1 << 36
+    st = tra.gemm_f32_variant(tra.NAIVE, M, 64, 0, None, 0, None, 64, C_ADDR, 64, None)
+    assert st == tra.TRA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("M,N", [(0, 5), (5, 0), (0, 0)])
+def test_empty_output_is_noop(M, N):
+    # nothing to compute: OK without touching any pointer (all NULL here)
+    assert tra.gemm_f32_variant(tra.MFMA, M, N, 7, None, 7, None, 5, None, 5, None) == tra.TRA_OK
+
+
+def test_python_matmul_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        tra.matmul(torch.zeros(2, 2), torch.zeros(2, 2))

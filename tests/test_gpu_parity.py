@@ -1,0 +1,333 @@
+"""Parity of every rung of the HIP ladder with the CPU oracle, through the
+C ABI (tiling_roofline_analysis_amd's ctypes binding of libtra_gemm.so).
+
+Acceptance:
+  * integer-pattern and small-integer inputs: the GPU's C equals the oracle's
+    C32 exactly (all partial sums are integers below 2^24, so every order of
+    summation gives the same value; compared with ==, so +0 and -0 are equal);
+  * floating-point inputs: |C_gpu - C64| <= 1e-5 * S per element, where C64
+    is the oracle's binary64 sum and S = sum_k |A_ik * B_kj|.
+Full-size shapes are checked on sampled entries the oracle computes one by
+one (whole rows and columns at tile edges plus random entries); the
+integer patterns are checked on every element through their period
+(C depends only on i mod 13 and j mod 7).
+"""
+from __future__ import annotations
+
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import tiling_roofline_analysis_amd as tra
+from tiling_roofline_analysis_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+RUNGS = [tra.NAIVE, tra.LDS_TILED, tra.REGBLOCK_DB, tra.MFMA]
+RUNG_IDS = ["naive", "lds_tiled", "regblock_db", "mfma"]
+C_SENTINEL = np.float32(12345.0)
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    tra.load()   # fails loudly if the HIP library is missing
+    return torch.device("cuda:0")
+
+
+def to_device(x: np.ndarray, ld: int, off: int, fill=np.nan):
+    """Flat device buffer holding row-major x with leading dimension ld,
+    starting `off` floats in; returns (tensor, address of x[0,0])."""
+    import torch
+    rows, cols = x.shape
+    n = off + max(rows * ld, 1)
+    host = np.full(n, np.float32(fill), np.float32)
+    if rows and cols:
+        host[off:off + rows * ld].reshape(rows, ld)[:, :cols] = x
+    t = torch.from_numpy(host).to("cuda:0")
+    return t, t.data_ptr() + 4 * off
+
+
+def run_gpu(variant, A, B, lda=None, ldb=None, ldc=None, offs=(0, 0, 0), stream=None,
+            c_init=C_SENTINEL):
+    """C = A x B on the GPU; returns (C (M x N), whole C buffer, ldc, off)."""
+    import torch
+    M, K = A.shape
+    N = B.shape[1]
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    tA, pA = to_device(A, lda, offs[0])
+    tB, pB = to_device(B, ldb, offs[1])
+    nC = offs[2] + max(M * ldc, 1)
+    tC = torch.full((nC,), float(c_init), dtype=torch.float32, device="cuda:0")
+    pC = tC.data_ptr() + 4 * offs[2]
+    s = stream if stream is not None else torch.cuda.current_stream()
+    st = tra.gemm_f32_variant(variant, M, N, K, pA, lda, pB, ldb, pC, ldc, s.cuda_stream)
+    assert st == tra.TRA_OK, tra.tra_status_string(st)
+    torch.cuda.synchronize()
+    buf = tC.cpu().numpy()
+    C = buf[offs[2]:offs[2] + M * ldc].reshape(M, ldc)[:, :N] if M else np.zeros((0, N), np.float32)
+    return C, buf, ldc, offs[2]
+
+
+def assert_exact(C, ref32, what):
+    bad = C != ref32
+    assert not bad.any(), (f"{what}: {int(bad.sum())} elements differ; first at "
+                           f"{np.argwhere(bad)[0]}: gpu {C[bad][0]} vs {ref32[bad][0]}")
+
+
+def assert_tol(C, c64, s64, what):
+    err = np.abs(C.astype(np.float64) - c64)
+    lim = TOL * s64
+    bad = err > lim
+    ratio = float(np.max(err / np.where(s64 > 0, s64, 1.0))) if err.size else 0.0
+    assert not bad.any(), (f"{what}: {int(bad.sum())} elements beyond 1e-5*S "
+                           f"(max |diff|/S = {ratio:.3e})")
+    return ratio
+
+
+@functools.lru_cache(maxsize=None)
+def workload_inputs(name):
+    return inputs.WORKLOADS[name].make()
+
+
+@functools.lru_cache(maxsize=None)
+def int_inputs(M, N, K):
+    return inputs.int_pattern_a(M, K), inputs.int_pattern_b(K, N)
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_full(name):
+    A, B = workload_inputs(name)
+    return oracle.gemm(A, B)
+
+
+# --- the configured small shapes, every element -------------------------------
+
+@pytest.mark.parametrize("name", ["int256", "const256", "int1024", "uniform1024"])
+@pytest.mark.parametrize("variant", RUNGS, ids=RUNG_IDS)
+def test_small_configs_full(variant, name):
+    log(f"[case] {tra.tra_gemm_variant_name(variant)} {name}")
+    A, B = workload_inputs(name)
+    ref = oracle_full(name)
+    C, *_ = run_gpu(variant, A, B)
+    w = inputs.WORKLOADS[name]
+    if w.kind in ("int", "const"):
+        # integer patterns are exact; the constant case is exact in the
+        # oracle but not for every binary32 summation order
+        if w.kind == "int":
+            assert_exact(C, ref.c32, name)
+        assert_tol(C, ref.c64, ref.s64, name)
+    else:
+        assert_tol(C, ref.c64, ref.s64, name)
+
+
+def test_constant_256_close_to_51_2():
+    A, B = workload_inputs("const256")
+    for v in RUNGS:
+        C, *_ = run_gpu(v, A, B)
+        assert np.all(np.abs(C.astype(np.float64) - 51.20000076293945) <= TOL * 51.20000076293945)
+
+
+# --- the configured large shapes ----------------------------------------------
+
+def edge_indices(n, extra=()):
+    cand = {0, 1, 31, 32, 63, 64, 127, 128, 255, 256, 511, 512, n // 2, n - 2, n - 1, *extra}
+    return sorted(i for i in cand if 0 <= i < n)
+
+
+def sample_entries(M, N, seed, n_random=20000):
+    rng = np.random.default_rng(seed)
+    rs, cs = [], []
+    for i in edge_indices(M)[:6] + edge_indices(M)[-3:]:
+        rs.append(np.full(N, i))
+        cs.append(np.arange(N))
+    for j in edge_indices(N)[:6] + edge_indices(N)[-3:]:
+        rs.append(np.arange(M))
+        cs.append(np.full(M, j))
+    rs.append(rng.integers(0, M, n_random))
+    cs.append(rng.integers(0, N, n_random))
+    return np.concatenate(rs), np.concatenate(cs)
+
+
+@pytest.mark.parametrize("name", ["normal4096", "ragged", "tall"])
+@pytest.mark.parametrize("variant", RUNGS, ids=RUNG_IDS)
+def test_large_configs_sampled(variant, name):
+    w = inputs.WORKLOADS[name]
+    log(f"[case] {tra.tra_gemm_variant_name(variant)} {name} {w.M}x{w.N}x{w.K} "
+        f"({tra.tra_gemm_describe(variant, w.M, w.N, w.K)})")
+    A, B = workload_inputs(name)
+    C, *_ = run_gpu(variant, A, B)
+    rows, cols = sample_entries(w.M, w.N, seed=w.M)
+    ref = oracle.gemm_entries(A, B, rows, cols)
+    assert_tol(C[rows, cols], ref.c64, ref.s64, name)
+    assert np.isfinite(C).all()
+
+
+@pytest.mark.parametrize("name", ["normal4096", "ragged", "tall"])
+@pytest.mark.parametrize("variant", RUNGS, ids=RUNG_IDS)
+def test_large_shapes_int_patterns_every_element(variant, name):
+    w = inputs.WORKLOADS[name]
+    log(f"[case] int patterns {tra.tra_gemm_variant_name(variant)} {w.M}x{w.N}x{w.K}")
+    A, B = int_inputs(w.M, w.N, w.K)
+    C, *_ = run_gpu(variant, A, B)
+    # the oracle's values on one period, then every element through it
+    ii, jj = np.meshgrid(np.arange(min(13, w.M)), np.arange(min(7, w.N)), indexing="ij")
+    per = oracle.gemm_entries(A, B, ii.ravel(), jj.ravel())
+    T = per.c32.reshape(ii.shape)
+    exp = T[np.arange(w.M)[:, None] % 13, np.arange(w.N)[None, :] % 7]
+    assert_exact(C, exp, f"int patterns {name}")
+    # and a sample directly from the oracle, not through the period
+    rows, cols = sample_entries(w.M, w.N, seed=1, n_random=2000)
+    direct = oracle.gemm_entries(A, B, rows, cols)
+    assert_exact(C[rows, cols], direct.c32, f"int patterns {name} (direct)")
+
+
+# --- tails, strides, alignment -------------------------------------------------
+
+EDGE_M = [1, 17, 33, 65, 129, 257]
+EDGE_K = [1, 2, 15, 16, 17, 31, 32, 33, 127, 129]
+
+
+@pytest.mark.parametrize("variant", RUNGS, ids=RUNG_IDS)
+def test_edge_sizes(variant):
+    rng = np.random.default_rng(21)
+    for M in EDGE_M:
+        for N in EDGE_M:
+            for K in EDGE_K:
+                A = rng.uniform(-1, 1, (M, K)).astype(np.float32)
+                B = rng.uniform(-1, 1, (K, N)).astype(np.float32)
+                ref = oracle.gemm(A, B)
+                C, *_ = run_gpu(variant, A, B)
+                assert_tol(C, ref.c64, ref.s64, f"{M}x{N}x{K}")
+                Ai = inputs.small_ints(M, K, M * 1000 + K)
+                Bi = inputs.small_ints(K, N, N * 1000 + K)
+                refi = oracle.gemm(Ai, Bi)
+                Ci, *_ = run_gpu(variant, Ai, Bi)
+                assert_exact(Ci, refi.c32, f"small ints {M}x{N}x{K}")
+
+
+# M=1300, N=5500 gives 6 x 43 = 258 tiles of 256 x 128, so the MFMA rung uses
+# its large tile here, with tails on every axis (1300 % 256, 5500 % 128, 203 % 16).
+LARGE_TILE_SHAPE = (1300, 5500, 203)
+
+
+@pytest.mark.parametrize("variant", RUNGS, ids=RUNG_IDS)
+def test_large_tile_with_tails(variant):
+    M, N, K = LARGE_TILE_SHAPE
+    if variant == tra.MFMA:
+        assert "tile=256x128x16" in tra.tra_gemm_describe(variant, M, N, K)
+    A = inputs.uniform(M, K, 77)
+    B = inputs.uniform(K, N, 78)
+    ref = oracle.gemm(A, B)
+    C, *_ = run_gpu(variant, A, B)
+    assert_tol(C, ref.c64, ref.s64, "large tile with tails")
+
+
+@pytest.mark.parametrize("layout", ["padded_aligned", "padded_misaligned"])
+@pytest.mark.parametrize("shape", [(300, 200, 150), LARGE_TILE_SHAPE])
+@pytest.mark.parametrize("variant", RUNGS, ids=RUNG_IDS)
+def test_strides_and_alignment(variant, shape, layout):
+    M, N, K = shape
+    def up4(x):
+        return (x + 3) // 4 * 4
+
+    if layout == "padded_aligned":     # vector-load path with padded rows
+        lda, ldb, ldc, offs = up4(K) + 4, up4(N) + 8, up4(N) + 4, (0, 0, 0)
+    else:                              # element-load path: odd strides, 4-byte offsets
+        lda, ldb, ldc, offs = K + 3, N + 5, N + 7, (1, 3, 1)
+    A = inputs.uniform(M, K, 5)
+    B = inputs.uniform(K, N, 6)
+    ref = oracle.gemm(A, B)
+    C, buf, ldc_, off = run_gpu(variant, A, B, lda, ldb, ldc, offs)
+    assert_tol(C, ref.c64, ref.s64, f"{layout} {shape}")
+    # nothing outside the first N columns of each row of C was written
+    full = buf[off:off + M * ldc_].reshape(M, ldc_)
+    assert np.all(full[:, N:] == C_SENTINEL)
+    assert np.all(buf[:off] == C_SENTINEL)
+
+
+@pytest.mark.parametrize("variant", RUNGS, ids=RUNG_IDS)
+def test_k_zero_writes_zeros(variant):
+    A = np.zeros((70, 0), np.float32)
+    B = np.zeros((0, 130), np.float32)
+    C, *_ = run_gpu(variant, A, B, lda=0, ldb=130, c_init=np.nan)
+    assert np.all(C == 0.0)
+
+
+@pytest.mark.parametrize("variant", RUNGS, ids=RUNG_IDS)
+def test_empty_output_untouched(variant):
+    import torch
+    c = torch.full((16,), 7.0, device="cuda:0")
+    assert tra.gemm_f32_variant(variant, 0, 4, 4, 0, 4, 0, 4, c.data_ptr(), 4, None) == tra.TRA_OK
+    assert tra.gemm_f32_variant(variant, 4, 0, 4, 0, 4, 0, 4, c.data_ptr(), 4, None) == tra.TRA_OK
+    torch.cuda.synchronize()
+    assert torch.all(c == 7.0)
+
+
+# --- cross-rung, determinism, streams, errors ----------------------------------
+
+def test_rungs_agree_bitwise_on_int_patterns_1024():
+    # every rung gives the same bits (the page reports max |diff| = 0 between
+    # its naive and tiled kernels on these inputs)
+    A, B = workload_inputs("int1024")
+    outs = [run_gpu(v, A, B)[0] for v in RUNGS]
+    for o in outs[1:]:
+        assert float(np.max(np.abs(o - outs[0]))) == 0.0
+    assert_exact(outs[0], oracle_full("int1024").c32, "int1024")
+
+
+@pytest.mark.parametrize("name", ["uniform1024", "ragged"])
+def test_mfma_deterministic(name):
+    A, B = workload_inputs(name)
+    first = run_gpu(tra.MFMA, A, B)[0]
+    for _ in range(3):
+        assert np.array_equal(run_gpu(tra.MFMA, A, B)[0].view(np.uint32), first.view(np.uint32))
+
+
+def test_auto_is_mfma():
+    A, B = workload_inputs("uniform1024")
+    a = run_gpu(tra.AUTO, A, B)[0]
+    m = run_gpu(tra.MFMA, A, B)[0]
+    assert np.array_equal(a.view(np.uint32), m.view(np.uint32))
+
+
+def test_non_default_stream_and_torch_wrapper():
+    import torch
+    A, B = workload_inputs("uniform1024")
+    ref = oracle_full("uniform1024")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        dA = torch.from_numpy(A).to("cuda:0", non_blocking=False)
+        dB = torch.from_numpy(B).to("cuda:0", non_blocking=False)
+        C = tra.matmul(dA, dB)
+    s.synchronize()
+    assert_tol(C.cpu().numpy(), ref.c64, ref.s64, "side stream")
+
+
+def test_invalid_call_leaves_c_untouched():
+    import torch
+    a = torch.ones((8, 8), device="cuda:0")
+    b = torch.ones((8, 8), device="cuda:0")
+    c = torch.full((8, 8), 3.0, device="cuda:0")
+    st = tra.gemm_f32_variant(tra.MFMA, 8, 8, 8, a.data_ptr(), 7, b.data_ptr(), 8,
+                              c.data_ptr(), 8, None)
+    assert st == tra.TRA_ERR_INVALID_ARG
+    st = tra.gemm_f32_variant(tra.MFMA, 8, 8, 8, a.data_ptr(), 8, b.data_ptr(), 8,
+                              a.data_ptr(), 8, None)
+    assert st == tra.TRA_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert torch.all(c == 3.0) and torch.all(a == 1.0)
+    with pytest.raises(ValueError):
+        tra.matmul(a[:, :7], b)       # inner dimensions differ

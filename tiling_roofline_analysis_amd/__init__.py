@@ -1,1 +1,158 @@
-"""MI355X-native single-precision GEMM (C = A x B, row-major) for gfx950."""
+"""MI355X-native single-precision GEMM (C = A x B, row-major) for gfx950.
+
+A thin ctypes binding of libtra_gemm.so, whose C ABI is declared in
+include/tra_gemm.h.  The functions here have the ABI's names and only
+marshal arguments: every step of the GEMM runs in the library's HIP kernels.
+There is no CPU fallback; if the library is missing, every call raises.
+
+Low-level calls take raw device addresses (ints) and a hipStream_t handle:
+
+    gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream) -> status
+    gemm_f32_variant(variant, M, N, K, A, lda, B, ldb, C, ldc, stream) -> status
+
+``matmul(A, B, C=None, variant=AUTO)`` is the torch-tensor convenience
+form: it checks the tensors, passes their device pointers and torch's
+current stream, and raises TraError on a non-OK status.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtra_gemm.so")
+
+# tra_status
+TRA_OK = 0
+TRA_ERR_INVALID_ARG = 1
+TRA_ERR_UNSUPPORTED = 2
+TRA_ERR_HIP = 3
+
+# tra_gemm_variant
+AUTO = 0
+NAIVE = 1
+LDS_TILED = 2
+REGBLOCK_DB = 3
+MFMA = 4
+VARIANTS = {"auto": AUTO, "naive": NAIVE, "lds_tiled": LDS_TILED,
+            "regblock_db": REGBLOCK_DB, "mfma": MFMA}
+LADDER = (NAIVE, LDS_TILED, REGBLOCK_DB, MFMA)
+
+ABI_FUNCTIONS = ("gemm_f32", "gemm_f32_variant", "tra_gemm_describe", "tra_status_string",
+                 "tra_gemm_variant_name", "tra_last_hip_error")
+
+
+class TraError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        msg = f"{what}: {tra_status_string(status)} (status {status})"
+        if status == TRA_ERR_HIP:
+            msg += f", hipError_t {tra_last_hip_error()}"
+        super().__init__(msg)
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libtra_gemm.so (built by __graft_entry__.build() or build.py)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, p, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.gemm_f32.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
+    lib.gemm_f32.restype = c_int
+    lib.gemm_f32_variant.argtypes = [c_int, i64, i64, i64, p, i64, p, i64, p, i64, p]
+    lib.gemm_f32_variant.restype = c_int
+    lib.tra_gemm_describe.argtypes = [c_int, i64, i64, i64, ctypes.c_char_p, ctypes.c_size_t]
+    lib.tra_gemm_describe.restype = c_int
+    lib.tra_status_string.argtypes = [c_int]
+    lib.tra_status_string.restype = ctypes.c_char_p
+    lib.tra_gemm_variant_name.argtypes = [c_int]
+    lib.tra_gemm_variant_name.restype = ctypes.c_char_p
+    lib.tra_last_hip_error.argtypes = []
+    lib.tra_last_hip_error.restype = c_int
+    _lib = lib
+    return lib
+
+
+# --- the ABI, one Python function per C function -----------------------------
+
+def gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return load().gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f32_variant(variant, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return load().gemm_f32_variant(variant, M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def tra_gemm_describe(variant: int, M: int, N: int, K: int) -> str:
+    buf = ctypes.create_string_buffer(256)
+    st = load().tra_gemm_describe(variant, M, N, K, buf, len(buf))
+    if st != TRA_OK:
+        raise TraError(st, "tra_gemm_describe")
+    return buf.value.decode()
+
+
+def tra_status_string(status: int) -> str:
+    return load().tra_status_string(status).decode()
+
+
+def tra_gemm_variant_name(variant: int) -> str:
+    return load().tra_gemm_variant_name(variant).decode()
+
+
+def tra_last_hip_error() -> int:
+    return load().tra_last_hip_error()
+
+
+# --- torch convenience --------------------------------------------------------
+
+def _check_operand(x, name):
+    import torch
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if x.dtype != torch.float32 or x.dim() != 2 or not x.is_cuda:
+        raise TypeError(f"{name} must be a 2-D float32 tensor on a GPU")
+    if x.size(0) > 1 and x.size(1) > 0 and x.stride(1) != 1:
+        raise ValueError(f"{name} must be row-major (unit column stride)")
+
+
+def _ld(x) -> int:
+    return x.stride(0) if x.size(0) > 1 else max(1, x.size(1))
+
+
+def matmul(A, B, C=None, variant: int = AUTO, stream=None):
+    """C = A @ B on the GPU through libtra_gemm.so; returns C.
+
+    A (M x K) and B (K x N) are float32 row-major tensors (row padding
+    allowed) on the same device; C, if given, is an M x N float32 row-major
+    tensor that is overwritten.  ``stream`` is a torch.cuda.Stream or None
+    for torch's current stream.
+    """
+    import torch
+    _check_operand(A, "A")
+    _check_operand(B, "B")
+    M, K = A.shape
+    if B.shape[0] != K:
+        raise ValueError(f"inner dimensions differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
+    N = B.shape[1]
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    else:
+        _check_operand(C, "C")
+        if tuple(C.shape) != (M, N):
+            raise ValueError(f"C must be {M} x {N}")
+    if B.device != A.device or C.device != A.device:
+        raise ValueError("A, B and C must be on the same device")
+    s = stream if stream is not None else torch.cuda.current_stream(A.device)
+    with torch.cuda.device(A.device):
+        st = gemm_f32_variant(variant, M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B),
+                              C.data_ptr(), _ld(C), s.cuda_stream)
+    if st != TRA_OK:
+        raise TraError(st, "gemm_f32_variant")
+    return C

@@ -1,0 +1,85 @@
+// gemm_lds_tiled.hip -- rung 2 of the ladder: LDS-staged square tiles.
+//
+// Page "GEMM kernel test code & optimization (1024^3 experiment)"
+// (teach-meaning.tistory.com/1513), sections "Shared-memory tiled GEMM",
+// "Tile concept" and "Tile loading step": a TILE x TILE workgroup computes a
+// TILE x TILE block of C.  The K axis is cut into TILE-wide slices; for each
+// slice every lane copies one element of A and one of B into on-chip memory
+// (zero outside the matrices), the group synchronises, every lane runs a
+// TILE-long dot product of a row of the A tile with a column of the B tile,
+// and the group synchronises again before the next slice overwrites the
+// tiles.  Each staged element is read TILE times from LDS instead of from
+// global memory (section "Key idea: reuse through shared memory").  Page
+// "[AutoMine++] #2 matmul trial and error" (velog.io/@levelstage/AutoMinepp2),
+// section "Breaking the memory bottleneck: Tiling", builds the same kernel
+// with TILE = 16 and no tail handling; tails here are zero-filled.
+//
+// gfx950 form: TILE = 32 and 1024 lanes (16 wave64s).  A wave holds two
+// tile rows of 32 lanes, so
+//   * staging reads two contiguous 128-byte row segments of A and of B per
+//     wave (coalesced), and writes 64 consecutive LDS words (no conflicts);
+//   * the dot product reads As[ty][k] (two addresses per wave, broadcast)
+//     and Bs[k][tx] (32 consecutive words, each read by two lanes), so the
+//     unpadded [32][32] layout has no bank conflicts.
+// The k order inside each element is 0..K-1, as in the naive rung.
+#include "gemm_internal.h"
+
+namespace tra {
+namespace {
+
+constexpr int kTile = 32;
+
+__global__ __launch_bounds__(kTile * kTile)
+void gemm_lds_tiled_f32(int64_t M, int64_t N, int64_t K,
+                        const float *__restrict__ A, int64_t lda,
+                        const float *__restrict__ B, int64_t ldb,
+                        float *__restrict__ C, int64_t ldc, int64_t tiles_n)
+{
+    __shared__ float As[kTile][kTile];
+    __shared__ float Bs[kTile][kTile];
+
+    const int tx = threadIdx.x, ty = threadIdx.y;
+    const int64_t bid = blockIdx.x;
+    const int64_t row = (bid / tiles_n) * kTile + ty;
+    const int64_t col = (bid % tiles_n) * kTile + tx;
+
+    float acc = 0.0f;
+    const int64_t slices = ceil_div(K, kTile);
+    for (int64_t t = 0; t < slices; ++t) {
+        const int64_t ka = t * kTile + tx;   // A element (row, ka)
+        const int64_t kb = t * kTile + ty;   // B element (kb, col)
+        As[ty][tx] = (row < M && ka < K) ? A[row * lda + ka] : 0.0f;
+        Bs[ty][tx] = (kb < K && col < N) ? B[kb * ldb + col] : 0.0f;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kTile; ++k) acc = fmaf(As[ty][k], Bs[k][tx], acc);
+        __syncthreads();
+    }
+    if (row < M && col < N) C[row * ldc + col] = acc;
+}
+
+}  // namespace
+
+LaunchPlan plan_lds_tiled(int64_t M, int64_t N, int64_t /*K*/) {
+    LaunchPlan p{};
+    p.kernel = "gemm_lds_tiled_f32";
+    p.bm = kTile;
+    p.bn = kTile;
+    p.bk = kTile;
+    p.grid = ceil_div(M, kTile) * ceil_div(N, kTile);
+    p.block = kTile * kTile;
+    p.lds_bytes = 2 * kTile * kTile * static_cast<int>(sizeof(float));
+    p.split_k = 1;
+    return p;
+}
+
+hipError_t launch_lds_tiled(const GemmArgs &a) {
+    const LaunchPlan p = plan_lds_tiled(a.M, a.N, a.K);
+    const int64_t tiles_n = ceil_div(a.N, kTile);
+    hipLaunchKernelGGL(gemm_lds_tiled_f32, dim3(static_cast<uint32_t>(p.grid)),
+                       dim3(kTile, kTile), 0, a.stream,
+                       a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, tiles_n);
+    return hipGetLastError();
+}
+
+}  // namespace tra

@@ -1,0 +1,150 @@
+// tra_gemm.hip -- the C-ABI entry points of libtra_gemm.so (declared in
+// include/tra_gemm.h): argument checks, choice of rung, launch on the
+// caller's stream.
+//
+// The argument checks follow the pages' interfaces: the CPU and SYCL
+// routines of page "[AutoMine++] #2 matmul trial and error"
+// (velog.io/@levelstage/AutoMinepp2, sections "Intuitive implementation (by
+// CPU)" and "Implementing with SYCL (iGPU)") refuse operands whose inner
+// dimensions differ -- here, leading dimensions too small for the stated
+// sizes -- and the kernels of page "GEMM kernel test code & optimization
+// (1024^3 experiment)" take restrict-qualified operands, so C may not
+// overlap A or B.  Errors come back as status codes; nothing throws across
+// the ABI.
+#include "tra_gemm.h"
+
+#include <cstdio>
+#include <cstring>
+
+#include "gemm_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+// Byte extent [lo, hi) of an r x c row-major view with leading dimension ld.
+struct Extent {
+    uintptr_t lo, hi;
+};
+
+// Returns false if the extent overflows.
+bool extent_of(const void *p, int64_t rows, int64_t cols, int64_t ld, Extent &e) {
+    if (rows <= 0 || cols <= 0) {
+        e.lo = e.hi = reinterpret_cast<uintptr_t>(p);
+        return true;
+    }
+    __int128 elems = static_cast<__int128>(rows - 1) * ld + cols;
+    __int128 bytes = elems * static_cast<__int128>(sizeof(float));
+    if (bytes > static_cast<__int128>(INT64_MAX)) return false;
+    e.lo = reinterpret_cast<uintptr_t>(p);
+    e.hi = e.lo + static_cast<uintptr_t>(bytes);
+    return e.hi >= e.lo;
+}
+
+bool overlaps(const Extent &a, const Extent &b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool valid_variant(int v) { return v >= TRA_GEMM_AUTO && v < TRA_GEMM_VARIANT_COUNT; }
+
+tra::LaunchPlan plan_of(int variant, int64_t M, int64_t N, int64_t K) {
+    switch (variant) {
+        case TRA_GEMM_NAIVE: return tra::plan_naive(M, N, K);
+        case TRA_GEMM_LDS_TILED: return tra::plan_lds_tiled(M, N, K);
+        case TRA_GEMM_REGBLOCK_DB: return tra::plan_regblock(M, N, K);
+        default: return tra::plan_mfma(M, N, K);   // AUTO and MFMA
+    }
+}
+
+// Host-side checks only; touches no device.  On success M, N > 0.
+tra_status check_args(int variant, int64_t M, int64_t N, int64_t K, const float *A,
+                      int64_t lda, const float *B, int64_t ldb, const float *C, int64_t ldc,
+                      bool &noop) {
+    noop = false;
+    if (!valid_variant(variant)) return TRA_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0) return TRA_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) {
+        noop = true;
+        return TRA_OK;
+    }
+    if (C == nullptr || ldc < N) return TRA_ERR_INVALID_ARG;
+    Extent ec{};
+    if (!extent_of(C, M, N, ldc, ec)) return TRA_ERR_INVALID_ARG;
+    if (K > 0) {
+        if (A == nullptr || B == nullptr || lda < K || ldb < N) return TRA_ERR_INVALID_ARG;
+        Extent ea{}, eb{};
+        if (!extent_of(A, M, K, lda, ea) || !extent_of(B, K, N, ldb, eb))
+            return TRA_ERR_INVALID_ARG;
+        if (overlaps(ec, ea) || overlaps(ec, eb)) return TRA_ERR_INVALID_ARG;
+    }
+    const tra::LaunchPlan p = plan_of(variant, M, N, K);
+    if (p.grid <= 0 || p.grid > tra::kMaxGrid) return TRA_ERR_UNSUPPORTED;
+    return TRA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tra_status gemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K, const float *A,
+                            int64_t lda, const float *B, int64_t ldb, float *C, int64_t ldc,
+                            void *stream) {
+    bool noop = false;
+    const tra_status st = check_args(variant, M, N, K, A, lda, B, ldb, C, ldc, noop);
+    if (st != TRA_OK || noop) return st;
+
+    tra::GemmArgs a{M, N, K, A, lda, B, ldb, C, ldc, static_cast<hipStream_t>(stream)};
+    hipError_t err;
+    switch (variant) {
+        case TRA_GEMM_NAIVE: err = tra::launch_naive(a); break;
+        case TRA_GEMM_LDS_TILED: err = tra::launch_lds_tiled(a); break;
+        case TRA_GEMM_REGBLOCK_DB: err = tra::launch_regblock(a); break;
+        default: err = tra::launch_mfma(a); break;   // AUTO and MFMA
+    }
+    if (err != hipSuccess) {
+        g_last_hip_error = static_cast<int>(err);
+        return TRA_ERR_HIP;
+    }
+    return TRA_OK;
+}
+
+tra_status gemm_f32(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                    const float *B, int64_t ldb, float *C, int64_t ldc, void *stream) {
+    return gemm_f32_variant(TRA_GEMM_AUTO, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+tra_status tra_gemm_describe(int variant, int64_t M, int64_t N, int64_t K, char *buf,
+                             size_t len) {
+    if (!valid_variant(variant) || M < 0 || N < 0 || K < 0) return TRA_ERR_INVALID_ARG;
+    if (buf == nullptr) return len == 0 ? TRA_OK : TRA_ERR_INVALID_ARG;
+    if (len == 0) return TRA_OK;
+    const tra::LaunchPlan p = plan_of(variant, M, N, K);
+    std::snprintf(buf, len,
+                  "variant=%s kernel=%s tile=%dx%dx%d grid=%lld block=%d lds_bytes=%d split_k=%d",
+                  tra_gemm_variant_name(variant), p.kernel, p.bm, p.bn, p.bk,
+                  static_cast<long long>(p.grid), p.block, p.lds_bytes, p.split_k);
+    return TRA_OK;
+}
+
+const char *tra_status_string(int status) {
+    switch (status) {
+        case TRA_OK: return "ok";
+        case TRA_ERR_INVALID_ARG: return "invalid argument";
+        case TRA_ERR_UNSUPPORTED: return "unsupported";
+        case TRA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown";
+    }
+}
+
+const char *tra_gemm_variant_name(int variant) {
+    switch (variant) {
+        case TRA_GEMM_AUTO: return "auto";
+        case TRA_GEMM_NAIVE: return "naive";
+        case TRA_GEMM_LDS_TILED: return "lds_tiled";
+        case TRA_GEMM_REGBLOCK_DB: return "regblock_db";
+        case TRA_GEMM_MFMA: return "mfma";
+        default: return "unknown";
+    }
+}
+
+int tra_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"
