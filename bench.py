@@ -128,6 +128,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ladder", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy 5 times (scales HBM counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -178,6 +180,19 @@ def main():
         del dA, dB, dC
         torch.cuda.empty_cache()
         return out
+
+    if args.copy_calibration:
+        # A plain device-to-device copy of known size: 256 MiB read, 256 MiB
+        # written per launch.  Profilers' FETCH_SIZE / WRITE_SIZE readings of
+        # this kernel calibrate the same counters on the GEMM kernels.
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[copy-calibration] 5 x copy of {src.numel() * 4} bytes")
+        del src, dst
+        torch.cuda.empty_cache()
 
     t_wall = time.perf_counter()
     prim = measure(PRIMARY, args.steps, args.warmup, not args.no_ladder)
