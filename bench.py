@@ -18,7 +18,6 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import statistics
@@ -31,40 +30,10 @@ sys.path.insert(0, ROOT)
 METRIC = "FP32 GEMM TFLOP/s and % of roofline at 1024³ and 4096³, 1× MI355X"
 PRIMARY = "uniform1024"
 SECONDARY = "normal4096"
-PROFILES = os.path.join(ROOT, "profiles")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def source_digest() -> str:
-    """sha256 of the HIP sources of the MFMA rung (identifies the kernel build
-    that a stored counter reading belongs to)."""
-    h = hashlib.sha256()
-    for f in ("gemm_mfma.hip", "gemm_internal.h"):
-        with open(os.path.join(ROOT, "tiling_roofline_analysis_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
-def stored_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary for
-    this workload, if it was taken on the current kernel sources, else None."""
-    path = os.path.join(PROFILES, f"traffic_gemm_mfma_f32_{workload}.txt")
-    if not os.path.exists(path):
-        return None
-    kv = {}
-    for line in open(path):
-        if "=" in line and not line.lstrip().startswith("#"):
-            k, v = line.split("=", 1)
-            kv[k.strip()] = v.strip()
-    if kv.get("source_digest") != source_digest():
-        return None
-    try:
-        return float(kv["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
 
 
 def time_variant(tra, torch, variant, w, dA, dB, dC, steps, warmup):
@@ -142,6 +111,7 @@ def main():
     import tiling_roofline_analysis_amd as tra
     from tiling_roofline_analysis_amd import inputs
     from tiling_roofline_analysis_amd import roofline as rl
+    from tiling_roofline_analysis_amd.profiling import source_digest, stored_traffic
 
     if not os.path.exists(tra.LIB_PATH):
         import __graft_entry__
