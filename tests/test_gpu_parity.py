@@ -218,28 +218,48 @@ def test_edge_sizes(variant):
                 assert_exact(Ci, refi.c32, f"small ints {M}x{N}x{K}")
 
 
-# M=1300, N=5500 gives 6 x 43 = 258 tiles of 256 x 128, so the MFMA rung uses
-# its large tile here, with tails on every axis (1300 % 256, 5500 % 128, 203 % 16).
-LARGE_TILE_SHAPE = (1300, 5500, 203)
+# Shapes that send the MFMA rung to each of its tile shapes, with tails on
+# every axis: (M, N, K, expected tile).
+MFMA_TILE_SHAPES = [
+    (4000, 4200, 203, "tile=128x128x16"),   # 32 x 33 = 1056 tiles of 128 x 128
+    (1500, 1500, 77, "tile=64x64x64"),      # 576 tiles of 64 x 64
+    (200, 300, 4100, "tile=64x64x64"),      # long K
+    (300, 500, 203, "tile=64x64x32"),       # few tiles, short K
+]
 
 
-@pytest.mark.parametrize("variant", RUNGS, ids=RUNG_IDS)
-def test_large_tile_with_tails(variant):
-    M, N, K = LARGE_TILE_SHAPE
-    if variant == tra.MFMA:
-        assert "tile=256x128x16" in tra.tra_gemm_describe(variant, M, N, K)
+@functools.lru_cache(maxsize=None)
+def tile_shape_case(M, N, K):
     A = inputs.uniform(M, K, 77)
     B = inputs.uniform(K, N, 78)
-    ref = oracle.gemm(A, B)
+    return A, B, oracle.gemm(A, B)
+
+
+@pytest.mark.parametrize("shape", MFMA_TILE_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}x{s[2]}")
+@pytest.mark.parametrize("variant", RUNGS, ids=RUNG_IDS)
+def test_tile_shapes_with_tails(variant, shape):
+    M, N, K, tile = shape
+    if variant == tra.MFMA:
+        assert tile in tra.tra_gemm_describe(variant, M, N, K)
+    A, B, ref = tile_shape_case(M, N, K)
     C, *_ = run_gpu(variant, A, B)
-    assert_tol(C, ref.c64, ref.s64, "large tile with tails")
+    assert_tol(C, ref.c64, ref.s64, f"{M}x{N}x{K}")
+
+
+@functools.lru_cache(maxsize=None)
+def stride_case(M, N, K):
+    A = inputs.uniform(M, K, 5)
+    B = inputs.uniform(K, N, 6)
+    return A, B, oracle.gemm(A, B)
 
 
 @pytest.mark.parametrize("layout", ["padded_aligned", "padded_misaligned"])
-@pytest.mark.parametrize("shape", [(300, 200, 150), LARGE_TILE_SHAPE])
+@pytest.mark.parametrize("shape", [(300, 200, 150), (4000, 4200, 203), (1500, 1500, 77)],
+                         ids=lambda s: f"{s[0]}x{s[1]}x{s[2]}")
 @pytest.mark.parametrize("variant", RUNGS, ids=RUNG_IDS)
 def test_strides_and_alignment(variant, shape, layout):
     M, N, K = shape
+
     def up4(x):
         return (x + 3) // 4 * 4
 
@@ -247,9 +267,7 @@ def test_strides_and_alignment(variant, shape, layout):
         lda, ldb, ldc, offs = up4(K) + 4, up4(N) + 8, up4(N) + 4, (0, 0, 0)
     else:                              # element-load path: odd strides, 4-byte offsets
         lda, ldb, ldc, offs = K + 3, N + 5, N + 7, (1, 3, 1)
-    A = inputs.uniform(M, K, 5)
-    B = inputs.uniform(K, N, 6)
-    ref = oracle.gemm(A, B)
+    A, B, ref = stride_case(M, N, K)
     C, buf, ldc_, off = run_gpu(variant, A, B, lda, ldb, ldc, offs)
     assert_tol(C, ref.c64, ref.s64, f"{layout} {shape}")
     # nothing outside the first N columns of each row of C was written
