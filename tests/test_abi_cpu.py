@@ -55,11 +55,11 @@ def test_describe_plans():
     d = tra.tra_gemm_describe(tra.MFMA, 4096, 4096, 4096)
     assert "gemm_mfma_f32" in d and "tile=128x128x16" in d and "grid=1024" in d
     d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 1024)
-    assert "tile=64x64x32" in d and "grid=256" in d and "block=1024" in d
+    assert "tile=64x64x64" in d and "grid=256" in d and "block=512" in d
     d = tra.tra_gemm_describe(tra.MFMA, 16384, 64, 16384)
     assert "tile=64x64x64" in d and "grid=256" in d
     d = tra.tra_gemm_describe(tra.MFMA, 3000, 2049, 1531)
-    assert "tile=64x64x64" in d and "grid=1551" in d
+    assert "tile=64x64x32" in d and "grid=1551" in d and "block=256" in d
     d = tra.tra_gemm_describe(tra.NAIVE, 1024, 1024, 1024)
     assert "gemm_naive_f32" in d and "grid=4096" in d and "block=256" in d
     d = tra.tra_gemm_describe(tra.LDS_TILED, 1024, 1024, 1024)

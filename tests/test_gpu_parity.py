@@ -222,9 +222,9 @@ def test_edge_sizes(variant):
 # every axis: (M, N, K, expected tile).
 MFMA_TILE_SHAPES = [
     (4000, 4200, 203, "tile=128x128x16"),   # 32 x 33 = 1056 tiles of 128 x 128
-    (1500, 1500, 77, "tile=64x64x64"),      # 576 tiles of 64 x 64
+    (1500, 1500, 77, "tile=64x64x32"),      # 576 tiles of 64 x 64, short K
     (200, 300, 4100, "tile=64x64x64"),      # long K
-    (300, 500, 203, "tile=64x64x32"),       # few tiles, short K
+    (300, 500, 203, "tile=64x64x64"),       # few tiles
 ]
 
 

@@ -85,7 +85,10 @@ struct MfmaTile {
 };
 
 // X[row][col .. col+3] of a rows x cols row-major matrix, zero outside it.
-// Addresses are clamped into the matrix, so every load is valid; no branches.
+// Addresses are clamped into the matrix, so every load is valid, and the
+// zero is applied with an AND mask on the loaded bits: the loads are
+// unconditional (a select would let the compiler predicate each load behind
+// a branch and wait for it).
 __device__ __forceinline__ float4 load4_clamped(const float *X, int64_t ld, int64_t row,
                                                 int64_t col, int64_t rows, int64_t cols) {
     const bool rok = row < rows;
@@ -95,7 +98,8 @@ __device__ __forceinline__ float4 load4_clamped(const float *X, int64_t ld, int6
     for (int e = 0; e < 4; ++e) {
         const int64_t c = col + e;
         const float x = p[c < cols ? c : cols - 1];
-        v[e] = (rok && c < cols) ? x : 0.0f;
+        const unsigned keep = (rok && c < cols) ? 0xffffffffu : 0u;
+        v[e] = __uint_as_float(__float_as_uint(x) & keep);
     }
     return make_float4(v[0], v[1], v[2], v[3]);
 }
@@ -201,10 +205,11 @@ __device__ __forceinline__ void read_frags(const float *lds, int buf, int arow, 
         for (int j = 0; j < T::FN; ++j) fr.b[q][j] = bs[(kbase + q) * T::BST + bcol + 32 * j];
 }
 
-template <class T>
+// MFMA steps q0 .. q1-1 of one slice.
+template <class T, int q0, int q1>
 __device__ __forceinline__ void mfmas(const Frag<T> &fr, f32x16 (&acc)[T::FM][T::FN]) {
 #pragma unroll
-    for (int q = 0; q < T::HALF; ++q)
+    for (int q = q0; q < q1; ++q)
 #pragma unroll
         for (int i = 0; i < T::FM; ++i)
 #pragma unroll
@@ -248,15 +253,25 @@ __device__ __forceinline__ void k_loop(const Ctx<T> &c, float *lds, int arow, in
     __syncthreads();   // buffer 0 is rewritten in iteration 0
 
     // Iteration s: fragment set s % 2, register set of slice s+2 is
-    // (s+2) % NR.  `guarded` only in the last few iterations.
+    // (s+2) % NR.  `guarded` only in the last few iterations.  The order is
+    // pinned with scheduling barriers: the fragment reads, the first half of
+    // the MFMAs, the LDS stores and global loads, the second half of the
+    // MFMAs, the workgroup barrier.  (Left alone, the compiler sinks the
+    // MFMAs below the workgroup barrier, which makes them wait for the
+    // global loads and LDS stores instead of covering them.)
     auto step = [&](int64_t s, int fp, int rp, bool guarded) {
         if (!guarded || s + 1 < slices) read_frags<T>(lds, fp ^ 1, arow, bcol, kbase, fr[fp ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas<T, 0, T::HALF / 2>(fr[fp], acc);
+        __builtin_amdgcn_sched_barrier(0);
         if (!guarded || s + 2 < slices) {
             stage<T>(lds, fp, c.t, ra[rp], rb[rp]);
             if (!guarded) fetch<T, MODE>(c, (s + 2 + NR) * BK, ra[rp], rb[rp]);
             else if (s + 2 + NR < slices) fetch_any(s + 2 + NR, rp);
         }
-        mfmas<T>(fr[fp], acc);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas<T, T::HALF / 2, T::HALF>(fr[fp], acc);
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
     };
     const int64_t limit = MODE != kEdge ? full : slices;   // the main loop fetches below this
@@ -371,26 +386,27 @@ void gemm_mfma_f32(int64_t M, int64_t N, int64_t K,
     }
 }
 
-// Tile shapes (measured on MI355X; see the tile sweep in the design notes):
-//   Large   128x128x16, 4 waves of 64x64, two register sets: 2 workgroups per
-//           CU; for shapes with at least 4 such tiles per CU (4096^3).
-//   SmallK  64x64x64, 4 K groups of 4 waves of 32x32 (1024 lanes): long K or
-//           many small tiles (16384x64x16384, 3000x2049x1531).
-//   Small   64x64x32, 4 K groups: short K and about one tile per CU (1024^3).
+// Tile shapes (chosen by timing candidates on MI355X):
+//   Large  128x128x16, 4 waves of 64x64, two register sets, 2 workgroups per
+//          CU: shapes with at least 4 such tiles per CU (4096^3).
+//   Many   64x64x32, 4 waves of 32x32: many small tiles and short K
+//          (3000x2049x1531).
+//   Few    64x64x64, two K groups of 4 waves of 32x32 (8 waves): about one
+//          tile per CU or long K (1024^3, 16384x64x16384).
 using TileLarge = MfmaTile<128, 128, 16, 64, 64, 1, 2>;
-using TileSmallK = MfmaTile<64, 64, 64, 32, 32, 4, 2>;
-using TileSmall = MfmaTile<64, 64, 32, 32, 32, 4, 2>;
+using TileMany = MfmaTile<64, 64, 32, 32, 32, 1, 2>;
+using TileFew = MfmaTile<64, 64, 64, 32, 32, 2, 2>;
 
 constexpr int64_t kCUs = 256;
 
-enum class Shape { kLarge, kSmallK, kSmall };
+enum class Shape { kLarge, kMany, kFew };
 
 Shape pick(int64_t M, int64_t N, int64_t K) {
     const int64_t large_tiles = ceil_div(M, TileLarge::BM) * ceil_div(N, TileLarge::BN);
     if (large_tiles >= 4 * kCUs) return Shape::kLarge;
-    const int64_t small_tiles = ceil_div(M, TileSmall::BM) * ceil_div(N, TileSmall::BN);
-    if (K >= 4096 || small_tiles > 2 * kCUs) return Shape::kSmallK;
-    return Shape::kSmall;
+    const int64_t small_tiles = ceil_div(M, TileMany::BM) * ceil_div(N, TileMany::BN);
+    if (small_tiles > 2 * kCUs && K < 4096) return Shape::kMany;
+    return Shape::kFew;
 }
 
 template <class T>
@@ -422,16 +438,16 @@ hipError_t launch_tile(const GemmArgs &a) {
 LaunchPlan plan_mfma(int64_t M, int64_t N, int64_t K) {
     switch (pick(M, N, K)) {
         case Shape::kLarge: return plan_for<TileLarge>(M, N, "gemm_mfma_f32<128x128x16, 4 waves>");
-        case Shape::kSmallK: return plan_for<TileSmallK>(M, N, "gemm_mfma_f32<64x64x64, 4 K groups>");
-        default: return plan_for<TileSmall>(M, N, "gemm_mfma_f32<64x64x32, 4 K groups>");
+        case Shape::kMany: return plan_for<TileMany>(M, N, "gemm_mfma_f32<64x64x32, 4 waves>");
+        default: return plan_for<TileFew>(M, N, "gemm_mfma_f32<64x64x64, 2 K groups>");
     }
 }
 
 hipError_t launch_mfma(const GemmArgs &a) {
     switch (pick(a.M, a.N, a.K)) {
         case Shape::kLarge: return launch_tile<TileLarge>(a);
-        case Shape::kSmallK: return launch_tile<TileSmallK>(a);
-        default: return launch_tile<TileSmall>(a);
+        case Shape::kMany: return launch_tile<TileMany>(a);
+        default: return launch_tile<TileFew>(a);
     }
 }
 
