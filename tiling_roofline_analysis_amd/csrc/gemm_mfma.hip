@@ -347,19 +347,19 @@ void gemm_mfma_f32(int64_t M, int64_t N, int64_t K,
         }
         __syncthreads();
         if (grp > 0) return;
+        // A rolled loop over the groups keeps one group's values live at a
+        // time (unrolled, the compiler hoists every read and spills).
+#pragma unroll 1
+        for (int g = 1; g < KG; ++g) {
+            const float *src = lds + ((g - 1) * T::WAVES + wig) * PER_WAVE + lane;
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
+                for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int g = 1; g < KG; ++g) {
-                    const float *src = lds + ((g - 1) * T::WAVES + wig) * PER_WAVE + lane +
-                                       (i * FN + j) * 16 * 64;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][j][r] += src[r * 64];
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
+                    for (int r = 0; r < 16; ++r)
+                        acc[i][j][r] += src[((i * FN + j) * 16 + r) * 64];
+        }
     }
 
     // Epilogue: word r of accumulator (i, j) is row 8*(r/4) + 4*h + r%4,
@@ -374,6 +374,7 @@ void gemm_mfma_f32(int64_t M, int64_t N, int64_t K,
                 float *cp = C + (m0 + wm0 + 32 * i + 4 * h) * ldc + gn;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) cp[(8 * (r / 4) + (r % 4)) * ldc] = acc[i][j][r];
+                __builtin_amdgcn_sched_barrier(0);   // one block's addresses live at a time
                 continue;
             }
             if (gn >= N) continue;
@@ -391,11 +392,12 @@ void gemm_mfma_f32(int64_t M, int64_t N, int64_t K,
 //          CU: shapes with at least 4 such tiles per CU (4096^3).
 //   Many   64x64x32, 4 waves of 32x32: many small tiles and short K
 //          (3000x2049x1531).
-//   Few    64x64x64, two K groups of 4 waves of 32x32 (8 waves): about one
-//          tile per CU or long K (1024^3, 16384x64x16384).
+//   Few    64x64x64, four K groups of 2 waves of 32x64 (8 waves), one
+//          register set: about one tile per CU or long K (1024^3,
+//          16384x64x16384).
 using TileLarge = MfmaTile<128, 128, 16, 64, 64, 1, 2>;
 using TileMany = MfmaTile<64, 64, 32, 32, 32, 1, 2>;
-using TileFew = MfmaTile<64, 64, 64, 32, 32, 2, 2>;
+using TileFew = MfmaTile<64, 64, 64, 32, 64, 4, 1>;
 
 constexpr int64_t kCUs = 256;
 
@@ -439,7 +441,7 @@ LaunchPlan plan_mfma(int64_t M, int64_t N, int64_t K) {
     switch (pick(M, N, K)) {
         case Shape::kLarge: return plan_for<TileLarge>(M, N, "gemm_mfma_f32<128x128x16, 4 waves>");
         case Shape::kMany: return plan_for<TileMany>(M, N, "gemm_mfma_f32<64x64x32, 4 waves>");
-        default: return plan_for<TileFew>(M, N, "gemm_mfma_f32<64x64x64, 2 K groups>");
+        default: return plan_for<TileFew>(M, N, "gemm_mfma_f32<64x64x64, 4 K groups>");
     }
 }
 
