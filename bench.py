@@ -71,6 +71,47 @@ def time_variant(tra, torch, variant, w, dA, dB, dC, steps, warmup):
     return avg_ms, min(per), statistics.median(per)
 
 
+def measure_roofs(tra, torch):
+    """The two roofs measured on this device with the library's probes: HBM
+    bandwidth from a 1 GiB streaming copy (larger than the 256 MB last-level
+    cache), the FP32 MFMA and FP32 VALU (no packed FP32) peaks."""
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+
+    def timed(call, reps):
+        for _ in range(2):
+            call()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            st = call()
+            if st != tra.TRA_OK:
+                raise tra.TraError(st, "probe")
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    out = {}
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    t = timed(lambda: tra.tra_probe_copy_f32(n, src.data_ptr(), dst.data_ptr(), h), 5)
+    out["hbm_copy_tbps"] = round(tra.tra_probe_work(tra.PROBE_COPY, n) / t / 1e12, 3)
+    del src, dst
+    torch.cuda.empty_cache()
+    sink = torch.empty(tra.PROBE_SINK_FLOATS, dtype=torch.float32, device="cuda:0")
+    it = 20000
+    t = timed(lambda: tra.tra_probe_mfma_f32(it, sink.data_ptr(), h), 3)
+    out["mfma_fp32_tflops"] = round(tra.tra_probe_work(tra.PROBE_MFMA, it) / t / 1e12, 2)
+    it = 100000
+    t = timed(lambda: tra.tra_probe_fma_f32(it, sink.data_ptr(), h), 3)
+    out["valu_fp32_tflops"] = round(tra.tra_probe_work(tra.PROBE_FMA, it) / t / 1e12, 2)
+    out["ridge_flop_per_byte"] = round(out["mfma_fp32_tflops"] / out["hbm_copy_tbps"], 2)
+    return out
+
+
 def cpu_baseline(w):
     """The CPU oracle on the full headline product, on the host's cores."""
     import oracle
@@ -97,6 +138,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ladder", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-roofs", action="store_true", help="skip the roof probes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy 5 times (scales HBM counters)")
     args = ap.parse_args()
@@ -141,11 +183,10 @@ def main():
                 a2, m2, md2 = time_variant(tra, torch, v, w, dA, dB, dC, st, 1)
                 r2 = rl.gemm_roofline(w.M, w.N, w.K, a2 * 1e-3)
                 name_v = tra.tra_gemm_variant_name(v)
-                peak = rl.PEAK_FP32_MFMA_TFLOPS if v == tra.MFMA else rl.PEAK_FP32_VALU_TFLOPS
                 out["ladder"][name_v] = {
                     "ms": round(a2, 5), "tflops": round(r2["tflops"], 3),
                     "frac_of_fp32_peak": round(r2["tflops"] / rl.PEAK_FP32_MFMA_TFLOPS, 4),
-                    "frac_of_unit_peak": round(r2["tflops"] / peak, 4), "steps": st}
+                    "unit": "mfma" if v == tra.MFMA else "valu", "steps": st}
                 log(f"[{name}] {name_v:12s} {a2 * 1e3:10.2f} us  {r2['tflops']:8.2f} TFLOP/s")
         del dA, dB, dC
         torch.cuda.empty_cache()
@@ -169,6 +210,15 @@ def main():
     sec = None if args.no_secondary else measure(SECONDARY, args.steps, args.warmup,
                                                  not args.no_ladder)
     gpu_wall = time.perf_counter() - t_wall
+    roofs = None
+    if not args.no_roofs:
+        roofs = measure_roofs(tra, torch)
+        log(f"[roofs] measured: {roofs}")
+        # each rung against the measured roof of the unit it runs on
+        for m in (prim, sec):
+            for entry in (m or {}).get("ladder", {}).values():
+                roof = roofs["mfma_fp32_tflops" if entry["unit"] == "mfma" else "valu_fp32_tflops"]
+                entry["frac_of_measured_unit_roof"] = round(entry["tflops"] / roof, 4)
 
     def roofline_obj(m, workload):
         rep = m["rep"]
@@ -200,6 +250,7 @@ def main():
             "algorithmic_bytes": prim["rep"]["bytes"],
             "source_digest": source_digest(), "gpu_wall_s": round(gpu_wall, 2),
             "device": torch.cuda.get_device_name(0),
+            "measured_roofs": roofs,
         },
     }
     if prim["ladder"]:

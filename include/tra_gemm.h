@@ -134,6 +134,43 @@ TRA_API tra_status gemm_f32_variant(int variant,
 TRA_API tra_status tra_gemm_describe(int variant, int64_t M, int64_t N, int64_t K,
                              char *buf, size_t len);
 
+/*
+ * Measurement probes: the two roofs of the roofline model measured on the
+ * device (page "Roofline & Tiling notes", legato-user-group.github.io/
+ * tensor2silicon-lab/week04/researchers/jaehyeong: performance is bounded
+ * by min(peak flops, bandwidth x arithmetic intensity); its section 1 uses a
+ * vector add as the example with no reuse).  Each call enqueues one kernel
+ * on `stream` and returns; time it with events.  tra_probe_work() gives the
+ * work one call does: bytes moved for TRA_PROBE_COPY (amount = n), flops
+ * for TRA_PROBE_MFMA and TRA_PROBE_FMA (amount = iters); -1 for an unknown
+ * probe or a negative amount.
+ *
+ *   tra_probe_copy_f32  dst[i] = src[i] for i < n (float4 stream; src and
+ *                       dst 16-byte aligned and not overlapping, else
+ *                       TRA_ERR_INVALID_ARG).  Use buffers larger than the
+ *                       256 MB last-level cache to measure HBM.
+ *   tra_probe_mfma_f32  TRA_PROBE_BLOCKS workgroups of 4 waves, each wave
+ *                       `iters` rounds of 4 independent FP32 MFMAs
+ *                       (v_mfma_f32_32x32x2_f32) from registers.
+ *   tra_probe_fma_f32   the same grid, each lane `iters` rounds of 8
+ *                       independent v_fma_f32.
+ * The compute probes write TRA_PROBE_SINK_FLOATS floats of no meaning to
+ * `sink` (device memory owned by the caller).
+ */
+typedef enum tra_probe {
+    TRA_PROBE_COPY = 0,
+    TRA_PROBE_MFMA = 1,
+    TRA_PROBE_FMA = 2
+} tra_probe;
+
+#define TRA_PROBE_BLOCKS 1024
+#define TRA_PROBE_SINK_FLOATS (TRA_PROBE_BLOCKS * 256)
+
+TRA_API double tra_probe_work(int probe, int64_t amount);
+TRA_API tra_status tra_probe_copy_f32(int64_t n, const float *src, float *dst, void *stream);
+TRA_API tra_status tra_probe_mfma_f32(int64_t iters, float *sink, void *stream);
+TRA_API tra_status tra_probe_fma_f32(int64_t iters, float *sink, void *stream);
+
 /* Static strings for a status or variant value ("unknown" otherwise). */
 TRA_API const char *tra_status_string(int status);
 TRA_API const char *tra_gemm_variant_name(int variant);

@@ -120,6 +120,29 @@ def test_empty_output_is_noop(M, N):
     assert tra.gemm_f32_variant(tra.MFMA, M, N, 7, None, 7, None, 5, None, 5, None) == tra.TRA_OK
 
 
+def test_probe_work_formulas():
+    assert tra.tra_probe_work(tra.PROBE_COPY, 1000) == 8000.0
+    # blocks x 4 waves x iters x 4 MFMAs x (2*32*32*2) flops
+    assert tra.tra_probe_work(tra.PROBE_MFMA, 10) == 1024 * 4 * 10 * 4 * 4096
+    # lanes x iters x 8 chains x 2 flops
+    assert tra.tra_probe_work(tra.PROBE_FMA, 10) == 1024 * 256 * 10 * 8 * 2
+    assert tra.tra_probe_work(9, 10) == -1.0
+    assert tra.tra_probe_work(tra.PROBE_COPY, -1) == -1.0
+
+
+def test_probe_invalid_arguments_rejected_on_host():
+    bad = tra.TRA_ERR_INVALID_ARG
+    assert tra.tra_probe_copy_f32(-1, A_ADDR, B_ADDR, None) == bad
+    assert tra.tra_probe_copy_f32(16, None, B_ADDR, None) == bad
+    assert tra.tra_probe_copy_f32(16, A_ADDR + 4, B_ADDR, None) == bad     # misaligned
+    assert tra.tra_probe_copy_f32(16, A_ADDR, A_ADDR + 32, None) == bad    # overlap
+    assert tra.tra_probe_copy_f32(0, None, None, None) == tra.TRA_OK
+    assert tra.tra_probe_mfma_f32(-1, C_ADDR, None) == bad
+    assert tra.tra_probe_mfma_f32(1, None, None) == bad
+    assert tra.tra_probe_fma_f32(-1, C_ADDR, None) == bad
+    assert tra.tra_probe_fma_f32(1, None, None) == bad
+
+
 def test_python_matmul_rejects_cpu_tensors():
     import torch
     with pytest.raises(TypeError):

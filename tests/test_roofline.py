@@ -55,9 +55,10 @@ def test_config_intensities(M, N, K, ai):
     assert rl.bound(rl.gemm_ai(M, N, K)) == "compute"
 
 
-def test_valu_peak_is_half_of_mfma_peak():
-    assert rl.PEAK_FP32_VALU_TFLOPS == pytest.approx(78.6432)
-    assert rl.PEAK_FP32_VALU_TFLOPS * 2 == pytest.approx(rl.PEAK_FP32_MFMA_TFLOPS, rel=1e-3)
+def test_fp32_peak_from_unit_counts():
+    # 256 CUs x 2.4 GHz x 256 flop per clock per CU
+    assert rl.MI355X_CUS * rl.MI355X_CLOCK_GHZ * 256 / 1e3 == pytest.approx(
+        rl.PEAK_FP32_MFMA_TFLOPS, rel=1e-3)
 
 
 def test_gemm_roofline_report():

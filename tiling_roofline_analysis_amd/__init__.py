@@ -39,7 +39,15 @@ VARIANTS = {"auto": AUTO, "naive": NAIVE, "lds_tiled": LDS_TILED,
 LADDER = (NAIVE, LDS_TILED, REGBLOCK_DB, MFMA)
 
 ABI_FUNCTIONS = ("gemm_f32", "gemm_f32_variant", "tra_gemm_describe", "tra_status_string",
-                 "tra_gemm_variant_name", "tra_last_hip_error")
+                 "tra_gemm_variant_name", "tra_last_hip_error", "tra_probe_work",
+                 "tra_probe_copy_f32", "tra_probe_mfma_f32", "tra_probe_fma_f32")
+
+# tra_probe
+PROBE_COPY = 0
+PROBE_MFMA = 1
+PROBE_FMA = 2
+PROBE_BLOCKS = 1024
+PROBE_SINK_FLOATS = PROBE_BLOCKS * 256
 
 
 class TraError(RuntimeError):
@@ -76,6 +84,14 @@ def load() -> ctypes.CDLL:
     lib.tra_gemm_variant_name.restype = ctypes.c_char_p
     lib.tra_last_hip_error.argtypes = []
     lib.tra_last_hip_error.restype = c_int
+    lib.tra_probe_work.argtypes = [c_int, i64]
+    lib.tra_probe_work.restype = ctypes.c_double
+    lib.tra_probe_copy_f32.argtypes = [i64, p, p, p]
+    lib.tra_probe_copy_f32.restype = c_int
+    lib.tra_probe_mfma_f32.argtypes = [i64, p, p]
+    lib.tra_probe_mfma_f32.restype = c_int
+    lib.tra_probe_fma_f32.argtypes = [i64, p, p]
+    lib.tra_probe_fma_f32.restype = c_int
     _lib = lib
     return lib
 
@@ -108,6 +124,22 @@ def tra_gemm_variant_name(variant: int) -> str:
 
 def tra_last_hip_error() -> int:
     return load().tra_last_hip_error()
+
+
+def tra_probe_work(probe: int, amount: int) -> float:
+    return load().tra_probe_work(probe, amount)
+
+
+def tra_probe_copy_f32(n, src, dst, stream=None) -> int:
+    return load().tra_probe_copy_f32(n, src, dst, stream)
+
+
+def tra_probe_mfma_f32(iters, sink, stream=None) -> int:
+    return load().tra_probe_mfma_f32(iters, sink, stream)
+
+
+def tra_probe_fma_f32(iters, sink, stream=None) -> int:
+    return load().tra_probe_fma_f32(iters, sink, stream)
 
 
 # --- torch convenience --------------------------------------------------------

@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libtra_gemm.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["tra_gemm.hip", "gemm_naive.hip", "gemm_lds_tiled.hip", "gemm_regblock.hip",
-           "gemm_mfma.hip"]
+           "gemm_mfma.hip", "probes.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

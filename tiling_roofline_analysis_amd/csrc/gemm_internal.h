@@ -41,6 +41,9 @@ inline bool vec4_ok(const void *p, int64_t ld) {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0 && (ld & 3) == 0;
 }
 
+// Keeps a failed launch's hipError_t for tra_last_hip_error() (per thread).
+void record_hip_error(hipError_t err);
+
 LaunchPlan plan_naive(int64_t M, int64_t N, int64_t K);
 hipError_t launch_naive(const GemmArgs &a);
 

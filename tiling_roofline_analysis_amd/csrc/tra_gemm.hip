@@ -82,6 +82,8 @@ tra_status check_args(int variant, int64_t M, int64_t N, int64_t K, const float 
 
 }  // namespace
 
+void tra::record_hip_error(hipError_t err) { g_last_hip_error = static_cast<int>(err); }
+
 extern "C" {
 
 tra_status gemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K, const float *A,
@@ -100,7 +102,7 @@ tra_status gemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K, const 
         default: err = tra::launch_mfma(a); break;   // AUTO and MFMA
     }
     if (err != hipSuccess) {
-        g_last_hip_error = static_cast<int>(err);
+        tra::record_hip_error(err);
         return TRA_ERR_HIP;
     }
     return TRA_OK;

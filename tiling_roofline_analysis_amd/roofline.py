@@ -16,17 +16,16 @@ definition" (2.147e9 at 1024^3).
 
 MI355X figures (AMD's public specification, not the pages): 256 CUs at up
 to 2.4 GHz; dense FP32 157.3 TFLOP/s for both matrix (MFMA) and packed
-vector instructions; HBM3E 8 TB/s.
+vector instructions; HBM3E 8 TB/s.  The library's probes measure the roofs
+actually reachable on the device (HBM copy bandwidth, FP32 MFMA and FP32
+VALU rates; see tra_probe_* in include/tra_gemm.h).
 """
 from __future__ import annotations
 
 MI355X_CUS = 256
 MI355X_CLOCK_GHZ = 2.4
-# Dense FP32 MFMA peak: 256 CU x 2.4 GHz x 256 flop/clk/CU.
+# Dense FP32 peak, MFMA and packed VALU: 256 CU x 2.4 GHz x 256 flop/clk/CU.
 PEAK_FP32_MFMA_TFLOPS = 157.3
-# FP32 VALU without packed-FP32 instructions (this build disables them):
-# 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz.
-PEAK_FP32_VALU_TFLOPS = MI355X_CUS * 4 * 16 * 2 * MI355X_CLOCK_GHZ / 1e3   # 78.6
 HBM_TBPS = 8.0
 ELEM_BYTES = 4
 
