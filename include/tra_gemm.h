@@ -20,6 +20,12 @@
  * Ownership and memory: A, B and C are device pointers owned by the caller
  * (for example torch tensors on the current HIP device).  No entry point
  * allocates, frees or copies host memory; all work is enqueued on `stream`.
+ * Only the stream-K variant needs device scratch (partial tiles, see
+ * TRA_GEMM_MFMA_STREAMK): gemm_f32_variant_ws takes it from the caller and
+ * allocates nothing; gemm_f32 and gemm_f32_variant use a workspace that the
+ * library allocates on first need for each (device, stream) pair and keeps
+ * until the process ends (it grows, after synchronising that stream, when a
+ * later call needs more).
  *
  * Asynchrony: gemm_f32 and gemm_f32_variant return once the kernels are
  * enqueued on `stream` (a hipStream_t; NULL means the null stream of the
@@ -73,18 +79,35 @@ typedef enum tra_status {
  *                double-buffered LDS with register prefetch (VALU FMA).
  *   MFMA         CDNA matrix-core kernel on binary32 inputs
  *                (v_mfma_f32_32x32x2_f32), double-buffered LDS, tile shape
- *                chosen from the problem shape.
- *   AUTO         the library's choice for the shape (currently MFMA).
+ *                chosen from the problem shape; one tile per workgroup.
+ *   MFMA_STREAMK the MFMA kernel with the tile count decoupled from the
+ *                workgroup count.  When the tiles do not fill whole waves
+ *                of resident workgroups (the tile-size versus occupancy
+ *                trade-off of page "Roofline & Tiling notes",
+ *                legato-user-group.github.io/tensor2silicon-lab/week04/
+ *                researchers/jaehyeong, key points), the last partial wave
+ *                plus one full wave of tiles is cut into K slices and shared
+ *                out evenly over one wave of workgroups (the stream-K
+ *                decomposition of Osama et al., "Stream-K: Work-centric
+ *                Parallel Decomposition for Dense Matrix-Matrix
+ *                Multiplication on the GPU", 2023).  Tiles split between
+ *                workgroups are summed by a second kernel in K order, so
+ *                results are deterministic.  Needs a device workspace of
+ *                tra_gemm_workspace_size() bytes; without a split it runs
+ *                the MFMA launch.
+ *   AUTO         the library's choice for the shape: MFMA, or MFMA_STREAMK
+ *                where a split is predicted to pay.
  */
 typedef enum tra_gemm_variant {
     TRA_GEMM_AUTO = 0,
     TRA_GEMM_NAIVE = 1,
     TRA_GEMM_LDS_TILED = 2,
     TRA_GEMM_REGBLOCK_DB = 3,
-    TRA_GEMM_MFMA = 4
+    TRA_GEMM_MFMA = 4,
+    TRA_GEMM_MFMA_STREAMK = 5
 } tra_gemm_variant;
 
-#define TRA_GEMM_VARIANT_COUNT 5
+#define TRA_GEMM_VARIANT_COUNT 6
 
 /*
  * gemm_f32: C = A x B with the library's choice of kernel (TRA_GEMM_AUTO).
@@ -104,7 +127,9 @@ typedef enum tra_gemm_variant {
  *
  * Returns TRA_OK, TRA_ERR_INVALID_ARG (negative size, ld too small, NULL
  * pointer where data is needed, C overlapping A or B), TRA_ERR_UNSUPPORTED
- * (the launch grid would exceed 2^31 - 1 workgroups) or TRA_ERR_HIP.
+ * (the launch grid would exceed 2^31 - 1 workgroups) or TRA_ERR_HIP (a
+ * launch failed, or the library's stream-K workspace could not be
+ * allocated).
  */
 TRA_API tra_status gemm_f32(int64_t M, int64_t N, int64_t K,
                     const float *A, int64_t lda,
@@ -124,12 +149,42 @@ TRA_API tra_status gemm_f32_variant(int variant,
                             void *stream);
 
 /*
+ * gemm_f32_variant_ws: as gemm_f32_variant, with device scratch supplied by
+ * the caller instead of the library's: `workspace` (16-byte aligned device
+ * memory on the current device, owned by the caller) of `workspace_bytes`
+ * bytes, at least tra_gemm_workspace_size() for the same variant and
+ * sizes.  It may be NULL when that size is 0.  Calls that share a workspace
+ * must be ordered (e.g. on one stream); it holds no state between calls.
+ * Allocates nothing.  A workspace that is too small or NULL when one is
+ * needed is TRA_ERR_INVALID_ARG.
+ */
+TRA_API tra_status gemm_f32_variant_ws(int variant,
+                               int64_t M, int64_t N, int64_t K,
+                               const float *A, int64_t lda,
+                               const float *B, int64_t ldb,
+                               float *C, int64_t ldc,
+                               void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/*
+ * tra_gemm_workspace_size: device scratch in bytes that gemm_f32_variant_ws
+ * needs for this variant and these sizes on the current device (0 for every
+ * variant except a stream-K split), written to *bytes.  Returns
+ * TRA_ERR_INVALID_ARG for an unknown variant, negative sizes or bytes ==
+ * NULL.
+ */
+TRA_API tra_status tra_gemm_workspace_size(int variant, int64_t M, int64_t N, int64_t K,
+                                   size_t *bytes);
+
+/*
  * tra_gemm_describe: writes a one-line, NUL-terminated description of the
  * launch that gemm_f32_variant(variant, M, N, K, ...) would make for
  * 16-byte-aligned operands with lda = K, ldb = N, ldc = N (kernel name, tile
- * shape, grid and block size) into buf[0 .. len-1].  Host-only; touches no
- * device.  Returns TRA_OK, or TRA_ERR_INVALID_ARG for an unknown variant,
- * negative sizes, or buf == NULL with len > 0.
+ * shape, grid and block size, stream-K tiles and workgroups, workspace
+ * bytes) into buf[0 .. len-1].  Launches nothing; the stream-K split is
+ * planned for the current device's CU count, or MI355X's 256 CUs when no
+ * device is present.  Returns TRA_OK, or TRA_ERR_INVALID_ARG for an
+ * unknown variant, negative sizes, or buf == NULL with len > 0.
  */
 TRA_API tra_status tra_gemm_describe(int variant, int64_t M, int64_t N, int64_t K,
                              char *buf, size_t len);

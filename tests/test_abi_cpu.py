@@ -67,6 +67,21 @@ def test_describe_plans():
     d = tra.tra_gemm_describe(tra.REGBLOCK_DB, 3000, 2049, 1531)
     assert "grid=408" in d   # 24 x 17 tiles of 128 x 128
     assert tra.tra_gemm_describe(tra.AUTO, 16, 16, 16).startswith("variant=auto")
+    # stream-K: 1551 tiles of 64 x 64 on 256 CUs x 2 workgroups leave a last
+    # wave of 15 tiles; their 15 x 48 slices go to 120 workgroups of 6 (an
+    # eighth of a tile each), with two partial tiles of 16 KiB per
+    # workgroup; the main launch adds 4 fixup chunks per shared tile
+    d = tra.tra_gemm_describe(tra.MFMA_STREAMK, 3000, 2049, 1531)
+    assert "stream_k_tiles=15" in d and "stream_k_wgs=120" in d
+    assert "workspace_bytes=3932160" in d and "grid=1596" in d
+    # whole waves of tiles: no split, no workspace
+    d = tra.tra_gemm_describe(tra.MFMA_STREAMK, 4096, 4096, 4096)
+    assert "stream_k_tiles=0" in d and "workspace_bytes=0" in d
+    # fewer tiles than a wave: all of them split (40 tiles x 4 slices over
+    # 80 workgroups of at least 2 slices)
+    d = tra.tra_gemm_describe(tra.MFMA_STREAMK, 300, 500, 203)
+    assert "stream_k_tiles=40" in d and "stream_k_wgs=80" in d
+    assert "stream_k_tiles=0" in tra.tra_gemm_describe(tra.MFMA, 3000, 2049, 1531)
     with pytest.raises(tra.TraError):
         tra.tra_gemm_describe(7, 1, 1, 1)
     with pytest.raises(tra.TraError):
@@ -90,7 +105,7 @@ INVALID = [
     (tra.MFMA, 4, 4, 4, A_ADDR, 4, B_ADDR, 4, A_ADDR + 16, 4),      # C overlaps A
     (tra.MFMA, 4, 4, 4, A_ADDR, 4, B_ADDR, 4, B_ADDR + 60, 4),      # C overlaps B's last word
     (tra.NAIVE, 4, 4, 4, A_ADDR, 4, B_ADDR, 4, B_ADDR - 4, 4),      # C's last word on B's first
-    (5, 4, 4, 4, A_ADDR, 4, B_ADDR, 4, C_ADDR, 4),                  # unknown variant
+    (6, 4, 4, 4, A_ADDR, 4, B_ADDR, 4, C_ADDR, 4),                  # unknown variant
     (-1, 4, 4, 4, A_ADDR, 4, B_ADDR, 4, C_ADDR, 4),                 # unknown variant
     (tra.MFMA, 1 << 40, 4, 4, A_ADDR, 1 << 40, B_ADDR, 4, C_ADDR, 4),   # extent overflow
 ]
@@ -147,3 +162,54 @@ def test_python_matmul_rejects_cpu_tensors():
     import torch
     with pytest.raises(TypeError):
         tra.matmul(torch.zeros(2, 2), torch.zeros(2, 2))
+
+
+def test_workspace_size():
+    assert tra.tra_gemm_workspace_size(tra.MFMA, 3000, 2049, 1531) == 0
+    assert tra.tra_gemm_workspace_size(tra.NAIVE, 3000, 2049, 1531) == 0
+    assert tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, 3000, 2049, 1531) == 2 * 120 * 64 * 64 * 4
+    assert tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, 4096, 4096, 4096) == 0
+    assert tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, 0, 2049, 1531) == 0
+    # K of one slice leaves nothing to split
+    assert tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, 3000, 2049, 32) == 0
+    for bad in [(6, 1, 1, 1), (tra.MFMA, -1, 1, 1), (tra.MFMA, 1, 1, -1)]:
+        with pytest.raises(tra.TraError):
+            tra.tra_gemm_workspace_size(*bad)
+    out = ctypes.c_size_t(0)
+    assert tra.load().tra_gemm_workspace_size(tra.MFMA, 1, 1, 1, None) == tra.TRA_ERR_INVALID_ARG
+
+
+def test_caller_workspace_checked_on_host():
+    M, N, K = 3000, 2049, 1531
+    A, B, C = 0x100000000, 0x200000000, 0x300000000
+    need = tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, M, N, K)
+    ws = 0x400000000
+    call = lambda w, n: tra.gemm_f32_variant_ws(tra.MFMA_STREAMK, M, N, K, A, K, B, N, C, N,
+                                                w, n, None)
+    assert call(None, need) == tra.TRA_ERR_INVALID_ARG       # needed but NULL
+    assert call(ws, need - 1) == tra.TRA_ERR_INVALID_ARG     # too small
+    assert call(ws + 4, need) == tra.TRA_ERR_INVALID_ARG     # not 16-byte aligned
+    # the ordinary argument checks apply too
+    assert tra.gemm_f32_variant_ws(tra.MFMA_STREAMK, M, N, K, None, K, B, N, C, N, ws, need,
+                                   None) == tra.TRA_ERR_INVALID_ARG
+    assert tra.gemm_f32_variant_ws(6, M, N, K, A, K, B, N, C, N, ws, need,
+                                   None) == tra.TRA_ERR_INVALID_ARG
+    # nothing to compute: OK with no workspace
+    assert tra.gemm_f32_variant_ws(tra.MFMA_STREAMK, 0, N, K, None, K, None, N, None, N, None,
+                                   0, None) == tra.TRA_OK
+
+
+@pytest.mark.parametrize("shape,rung", [
+    ((1024, 1024, 1024), "mfma"),          # 256 tiles on 256 CUs
+    ((4096, 4096, 4096), "mfma"),          # 1024 tiles, 4 a CU
+    ((3000, 2049, 1531), "mfma_streamk"),  # 1551 tiles: 6.06 a CU
+    ((4608, 4608, 4096), "mfma_streamk"),  # 1296 tiles: 5.06 a CU
+    ((3072, 3072, 3072), "mfma"),          # 2304 tiles: 9 a CU
+    ((3008, 2048, 1536), "mfma"),          # 1504 tiles: 5.875 a CU, 2% short
+    ((1500, 1500, 77), "mfma"),            # 3 slices of K: nothing to share
+    ((1152, 1152, 8192), "mfma_streamk"),  # 324 tiles of one workgroup a CU
+    ((16384, 64, 16384), "mfma"),          # 256 tiles
+])
+def test_auto_choice(shape, rung):
+    d = tra.tra_gemm_describe(tra.AUTO, *shape)
+    assert f"rung={rung} " in d, d

@@ -27,8 +27,9 @@ from tiling_roofline_analysis_amd import inputs
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-5
-RUNGS = [tra.NAIVE, tra.LDS_TILED, tra.REGBLOCK_DB, tra.MFMA]
-RUNG_IDS = ["naive", "lds_tiled", "regblock_db", "mfma"]
+# the four rungs of the ladder and the stream-K form of the MFMA rung
+RUNGS = [tra.NAIVE, tra.LDS_TILED, tra.REGBLOCK_DB, tra.MFMA, tra.MFMA_STREAMK]
+RUNG_IDS = ["naive", "lds_tiled", "regblock_db", "mfma", "mfma_streamk"]
 C_SENTINEL = np.float32(12345.0)
 
 
@@ -239,7 +240,7 @@ def tile_shape_case(M, N, K):
 @pytest.mark.parametrize("variant", RUNGS, ids=RUNG_IDS)
 def test_tile_shapes_with_tails(variant, shape):
     M, N, K, tile = shape
-    if variant == tra.MFMA:
+    if variant in (tra.MFMA, tra.MFMA_STREAMK):
         assert tile in tra.tra_gemm_describe(variant, M, N, K)
     A, B, ref = tile_shape_case(M, N, K)
     C, *_ = run_gpu(variant, A, B)

@@ -1,0 +1,139 @@
+"""The stream-K form of the MFMA rung on the GPU: the split of tiles over
+workgroups, the two-pass deterministic reduction, and the two ways to
+provide its workspace (the library's per-stream buffer and the caller's).
+Results are checked against the CPU oracle (exact on integer patterns,
+1e-5 * sum |A_ik B_kj| on floating point)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import tiling_roofline_analysis_amd as tra
+from tiling_roofline_analysis_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    tra.load()
+
+
+def dev(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda:0")
+
+
+def check_tol(C, ref, what):
+    err = np.abs(C.astype(np.float64) - ref.c64)
+    assert np.all(err <= TOL * ref.s64), f"{what}: max |diff|/S = {np.max(err / ref.s64):.3e}"
+
+
+# Shapes whose tiles do not fill whole waves, one per tile class (the split
+# each gets on 256 CUs): fewer tiles than a wave (every tile split), a last
+# partial wave of a few tiles split many ways, and the large-tile class.
+SPLIT_SHAPES = [
+    (300, 500, 203),      # 40 tiles x 4 slices over 80 workgroups: 2 partial sums a tile
+    (257, 129, 1000),     # 15 tiles x 16 slices over 120 workgroups: 8 a tile
+    (1500, 1500, 77),     # 576 tiles of 64 x 64: the last 64 over 96 workgroups
+    (3000, 2049, 1531),   # the ragged shape: its last 15 tiles over 120 workgroups
+    (4000, 4200, 203),    # 1056 tiles of 128 x 128: the last 32 over 208 workgroups
+]
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_split_shapes_match_oracle(shape):
+    import torch
+    M, N, K = shape
+    d = tra.tra_gemm_describe(tra.MFMA_STREAMK, M, N, K)
+    print(f"[case] stream-K {M}x{N}x{K} ({d})", flush=True)
+    assert "stream_k_tiles=0" not in d
+    A = inputs.uniform(M, K, 31)
+    B = inputs.uniform(K, N, 32)
+    C = tra.matmul(dev(A), dev(B), variant=tra.MFMA_STREAMK)
+    torch.cuda.synchronize()
+    C = C.cpu().numpy()
+    if M * N * K <= 400 * 600 * 1100:
+        check_tol(C, oracle.gemm(A, B), f"{M}x{N}x{K}")
+    else:
+        rng = np.random.default_rng(M)
+        rows = np.concatenate([rng.integers(0, M, 20000), np.arange(M), np.full(N, M - 1)])
+        cols = np.concatenate([rng.integers(0, N, 20000), np.full(M, N - 1), np.arange(N)])
+        ref = oracle.gemm_entries(A, B, rows, cols)
+        err = np.abs(C[rows, cols].astype(np.float64) - ref.c64)
+        assert np.all(err <= TOL * ref.s64)
+    # integer patterns: exact whatever the split
+    Ai, Bi = inputs.int_pattern_a(M, K), inputs.int_pattern_b(K, N)
+    Ci = tra.matmul(dev(Ai), dev(Bi), variant=tra.MFMA_STREAMK)
+    torch.cuda.synchronize()
+    ii, jj = np.meshgrid(np.arange(min(13, M)), np.arange(min(7, N)), indexing="ij")
+    per = oracle.gemm_entries(Ai, Bi, ii.ravel(), jj.ravel()).c32.reshape(ii.shape)
+    exp = per[np.arange(M)[:, None] % 13, np.arange(N)[None, :] % 7]
+    assert np.array_equal(Ci.cpu().numpy(), exp)
+
+
+def test_split_is_deterministic():
+    import torch
+    M, N, K = 1500, 1500, 77
+    A, B = dev(inputs.uniform(M, K, 3)), dev(inputs.uniform(K, N, 4))
+    first = tra.matmul(A, B, variant=tra.MFMA_STREAMK).clone()
+    for _ in range(5):
+        again = tra.matmul(A, B, variant=tra.MFMA_STREAMK)
+        torch.cuda.synchronize()
+        assert torch.equal(first, again)
+
+
+def test_caller_workspace_matches_library_workspace():
+    import torch
+    M, N, K = 3000, 2049, 1531
+    A, B = dev(inputs.uniform(M, K, 5)), dev(inputs.uniform(K, N, 6))
+    need = tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, M, N, K)
+    assert need > 0
+    ws = torch.full((need // 4,), float("nan"), device="cuda:0")
+    C1 = tra.matmul(A, B, variant=tra.MFMA_STREAMK, workspace=ws)
+    C2 = tra.matmul(A, B, variant=tra.MFMA_STREAMK)
+    torch.cuda.synchronize()
+    assert torch.equal(C1, C2)
+    # a workspace one byte short is refused before anything runs
+    with pytest.raises(tra.TraError):
+        tra.matmul(A, B, variant=tra.MFMA_STREAMK, workspace=torch.empty(need // 4 - 1,
+                                                                          device="cuda:0"))
+
+
+def test_library_workspace_grows_and_serves_several_streams():
+    import torch
+    small, large = (300, 500, 203), (4000, 4200, 203)
+    assert (tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, *small)
+            < tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, *large))
+    cases = {}
+    for M, N, K in (small, large):
+        A, B = inputs.int_pattern_a(M, K), inputs.int_pattern_b(K, N)
+        rows = np.arange(0, M, 7)
+        cols = np.arange(0, N, 5)
+        rr, cc = np.meshgrid(rows, cols, indexing="ij")
+        ref = oracle.gemm_entries(A, B, rr.ravel(), cc.ravel()).c32.reshape(rr.shape)
+        cases[(M, N, K)] = (dev(A), dev(B), rows, cols, ref)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    # small then large on one stream (the buffer grows), then both streams
+    for shape, stream in ((small, s1), (large, s1), (large, s2), (small, s2), (small, s1)):
+        A, B, rows, cols, ref = cases[shape]
+        with torch.cuda.stream(stream):
+            C = tra.matmul(A, B, variant=tra.MFMA_STREAMK)
+        stream.synchronize()
+        assert np.array_equal(C.cpu().numpy()[np.ix_(rows, cols)], ref), shape
+
+
+def test_auto_uses_the_split_where_it_pays():
+    import torch
+    M, N, K = 3000, 2049, 1531
+    assert "rung=mfma_streamk" in tra.tra_gemm_describe(tra.AUTO, M, N, K)
+    A, B = dev(inputs.uniform(M, K, 5)), dev(inputs.uniform(K, N, 6))
+    C1 = tra.matmul(A, B)
+    C2 = tra.matmul(A, B, variant=tra.MFMA_STREAMK)
+    torch.cuda.synchronize()
+    assert torch.equal(C1, C2)

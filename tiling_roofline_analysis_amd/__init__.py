@@ -9,6 +9,8 @@ Low-level calls take raw device addresses (ints) and a hipStream_t handle:
 
     gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream) -> status
     gemm_f32_variant(variant, M, N, K, A, lda, B, ldb, C, ldc, stream) -> status
+    gemm_f32_variant_ws(variant, M, N, K, A, lda, B, ldb, C, ldc,
+                        workspace, workspace_bytes, stream) -> status
 
 ``matmul(A, B, C=None, variant=AUTO)`` is the torch-tensor convenience
 form: it checks the tensors, passes their device pointers and torch's
@@ -34,11 +36,13 @@ NAIVE = 1
 LDS_TILED = 2
 REGBLOCK_DB = 3
 MFMA = 4
+MFMA_STREAMK = 5
 VARIANTS = {"auto": AUTO, "naive": NAIVE, "lds_tiled": LDS_TILED,
-            "regblock_db": REGBLOCK_DB, "mfma": MFMA}
+            "regblock_db": REGBLOCK_DB, "mfma": MFMA, "mfma_streamk": MFMA_STREAMK}
 LADDER = (NAIVE, LDS_TILED, REGBLOCK_DB, MFMA)
 
-ABI_FUNCTIONS = ("gemm_f32", "gemm_f32_variant", "tra_gemm_describe", "tra_status_string",
+ABI_FUNCTIONS = ("gemm_f32", "gemm_f32_variant", "gemm_f32_variant_ws",
+                 "tra_gemm_workspace_size", "tra_gemm_describe", "tra_status_string",
                  "tra_gemm_variant_name", "tra_last_hip_error", "tra_probe_work",
                  "tra_probe_copy_f32", "tra_probe_mfma_f32", "tra_probe_fma_f32")
 
@@ -76,6 +80,12 @@ def load() -> ctypes.CDLL:
     lib.gemm_f32.restype = c_int
     lib.gemm_f32_variant.argtypes = [c_int, i64, i64, i64, p, i64, p, i64, p, i64, p]
     lib.gemm_f32_variant.restype = c_int
+    lib.gemm_f32_variant_ws.argtypes = [c_int, i64, i64, i64, p, i64, p, i64, p, i64, p,
+                                        ctypes.c_size_t, p]
+    lib.gemm_f32_variant_ws.restype = c_int
+    lib.tra_gemm_workspace_size.argtypes = [c_int, i64, i64, i64,
+                                            ctypes.POINTER(ctypes.c_size_t)]
+    lib.tra_gemm_workspace_size.restype = c_int
     lib.tra_gemm_describe.argtypes = [c_int, i64, i64, i64, ctypes.c_char_p, ctypes.c_size_t]
     lib.tra_gemm_describe.restype = c_int
     lib.tra_status_string.argtypes = [c_int]
@@ -104,6 +114,20 @@ def gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
 
 def gemm_f32_variant(variant, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
     return load().gemm_f32_variant(variant, M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f32_variant_ws(variant, M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes,
+                        stream=None) -> int:
+    return load().gemm_f32_variant_ws(variant, M, N, K, A, lda, B, ldb, C, ldc, workspace,
+                                      workspace_bytes, stream)
+
+
+def tra_gemm_workspace_size(variant: int, M: int, N: int, K: int) -> int:
+    out = ctypes.c_size_t(0)
+    st = load().tra_gemm_workspace_size(variant, M, N, K, ctypes.byref(out))
+    if st != TRA_OK:
+        raise TraError(st, "tra_gemm_workspace_size")
+    return out.value
 
 
 def tra_gemm_describe(variant: int, M: int, N: int, K: int) -> str:
@@ -158,13 +182,15 @@ def _ld(x) -> int:
     return x.stride(0) if x.size(0) > 1 else max(1, x.size(1))
 
 
-def matmul(A, B, C=None, variant: int = AUTO, stream=None):
+def matmul(A, B, C=None, variant: int = AUTO, stream=None, workspace=None):
     """C = A @ B on the GPU through libtra_gemm.so; returns C.
 
     A (M x K) and B (K x N) are float32 row-major tensors (row padding
     allowed) on the same device; C, if given, is an M x N float32 row-major
     tensor that is overwritten.  ``stream`` is a torch.cuda.Stream or None
-    for torch's current stream.
+    for torch's current stream.  ``workspace`` (a contiguous device tensor
+    of at least tra_gemm_workspace_size() bytes) replaces the library's own
+    scratch for the stream-K variant.
     """
     import torch
     _check_operand(A, "A")
@@ -183,8 +209,15 @@ def matmul(A, B, C=None, variant: int = AUTO, stream=None):
         raise ValueError("A, B and C must be on the same device")
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
     with torch.cuda.device(A.device):
-        st = gemm_f32_variant(variant, M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B),
-                              C.data_ptr(), _ld(C), s.cuda_stream)
+        if workspace is None:
+            st = gemm_f32_variant(variant, M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B),
+                                  C.data_ptr(), _ld(C), s.cuda_stream)
+        else:
+            if not workspace.is_cuda or workspace.device != A.device or not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous tensor on A's device")
+            st = gemm_f32_variant_ws(variant, M, N, K, A.data_ptr(), _ld(A), B.data_ptr(),
+                                     _ld(B), C.data_ptr(), _ld(C), workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(), s.cuda_stream)
     if st != TRA_OK:
         raise TraError(st, "gemm_f32_variant")
     return C

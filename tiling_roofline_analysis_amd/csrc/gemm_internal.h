@@ -21,7 +21,8 @@ struct GemmArgs {
     hipStream_t stream;
 };
 
-// What a rung will launch for a shape (host-only, no device needed).
+// What a rung will launch for a shape (host side; the stream-K split reads
+// the current device's CU count and falls back to MI355X's without one).
 struct LaunchPlan {
     const char *kernel;   // kernel function name (as profilers print it)
     int bm, bn, bk;       // block tile of C and K step (1 for no tile)
@@ -29,6 +30,9 @@ struct LaunchPlan {
     int block;            // lanes per workgroup
     int lds_bytes;        // LDS per workgroup
     int split_k;          // K partitions (1 = none)
+    int64_t sk_tiles;     // tiles shared out by K slice (stream-K), 0 = none
+    int64_t sk_wgs;       // workgroups that run them
+    size_t workspace_bytes;   // device scratch for partial tiles
 };
 
 // Grid limit of one launch (workgroups in the x dimension).
@@ -53,8 +57,12 @@ hipError_t launch_lds_tiled(const GemmArgs &a);
 LaunchPlan plan_regblock(int64_t M, int64_t N, int64_t K);
 hipError_t launch_regblock(const GemmArgs &a);
 
-LaunchPlan plan_mfma(int64_t M, int64_t N, int64_t K);
-hipError_t launch_mfma(const GemmArgs &a);
+// stream_k: share the last partial wave of tiles out by K slice (needs
+// `ws`, at least plan_mfma(..).workspace_bytes bytes, when that is > 0).
+LaunchPlan plan_mfma(int64_t M, int64_t N, int64_t K, bool stream_k);
+hipError_t launch_mfma(const GemmArgs &a, bool stream_k, void *ws, size_t ws_bytes);
+// True where the stream-K split is expected to beat one tile per workgroup.
+bool prefer_stream_k(int64_t M, int64_t N, int64_t K);
 
 // XCD-aware remap of a linear workgroup id.  The dispatcher hands
 // workgroups to the 8 XCDs of an MI355X round-robin (id mod 8), and each

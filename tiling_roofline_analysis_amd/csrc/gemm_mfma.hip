@@ -44,15 +44,29 @@
 // Each global load has NR iterations to arrive and every LDS access of an
 // iteration overlaps that iteration's MFMAs.
 //
-// Global loads: whole tiles with 16-byte-aligned rows (base aligned, ld a
-// multiple of 4) use float4 loads without checks, whole tiles of unaligned
-// operands element loads without checks; edge tiles load elements at
-// clamped, always-valid addresses and select zero outside the matrices (no
-// branches).  Out-of-range elements are +0 in every sum.
+// Global loads: a tile that would cross row M or column N is moved back
+// inside the matrices (its rows and columns shared with the neighbouring
+// tile are not stored), so full slices load without checks: float4 loads
+// for 16-byte-aligned rows (base aligned, ld a multiple of 4), element
+// loads otherwise.  The slice that runs past K, and matrices smaller than a
+// tile, load elements at clamped, always-valid addresses with zero selected
+// outside the matrices (no branches); out-of-range elements are +0 in every
+// sum.
 //
 // Workgroup ids are remapped so each of the 8 XCDs runs a compact patch of
 // tiles (shared L2 traffic), in groups of 8 tile rows.
+//
+// Stream-K (gemm_mfma_f32_sk plus the fixup at the start of gemm_mfma_f32):
+// the tiles of the last partial wave are shared out by K slice over up to
+// one wave of workgroups and their partial sums added in K order by a
+// second launch (the decomposition of Osama et al., "Stream-K:
+// Work-centric Parallel Decomposition for Dense Matrix-Matrix
+// Multiplication on the GPU", 2023; the tile count versus CU count
+// trade-off is that of page "Roofline & Tiling notes", key points).
 #include "gemm_internal.h"
+
+#include <algorithm>
+#include <atomic>
 
 namespace tra {
 namespace {
@@ -115,14 +129,17 @@ struct Ctx {
     int t;
 };
 
-// How a slice is loaded from global memory.
-//   kVec     whole tile inside the matrices, 16-byte-aligned rows: float4
-//            loads, no checks;
-//   kScalar  whole tile inside, rows not 16-byte aligned: four element
-//            loads per group, no checks;
-//   kEdge    the tile crosses an edge of A or B: element loads at clamped
-//            addresses, zero selected outside.
-enum LoadMode { kVec = 0, kScalar = 1, kEdge = 2 };
+// How a slice is loaded from global memory.  A tile is always placed inside
+// the matrices when they are at least one tile large (see tile_origin), so
+// only the slice that runs past K and matrices smaller than a tile need
+// index checks.
+//   kVec      A and B rows 16-byte aligned at the tile: float4 loads;
+//   kVecA     A aligned, B not (ldb or the tile's first column not a
+//             multiple of 4): float4 loads of A, element loads of B;
+//   kScalar   element loads of both;
+//   kChecked  element loads at clamped addresses with zeros outside the
+//             matrices (the k tail slice, and tiles larger than the matrix).
+enum LoadMode { kVec = 0, kVecA = 1, kScalar = 2, kChecked = 3 };
 
 __device__ __forceinline__ float4 load4_scalar(const float *p) {
     return make_float4(p[0], p[1], p[2], p[3]);
@@ -138,7 +155,7 @@ __device__ __forceinline__ void fetch(const Ctx<T> &c, int64_t k0, float4 (&ra)[
         if (T::A_VEC % T::THREADS != 0 && f >= T::A_VEC) break;
         const int m = f / (T::BK / 4), kq = f % (T::BK / 4);
         const float *p = c.A + (c.m0 + m) * c.lda + k0 + 4 * kq;
-        if (MODE == kVec) ra[r] = *reinterpret_cast<const float4 *>(p);
+        if (MODE == kVec || MODE == kVecA) ra[r] = *reinterpret_cast<const float4 *>(p);
         else if (MODE == kScalar) ra[r] = load4_scalar(p);
         else ra[r] = load4_clamped(c.A, c.lda, c.m0 + m, k0 + 4 * kq, c.M, c.K);
     }
@@ -149,7 +166,7 @@ __device__ __forceinline__ void fetch(const Ctx<T> &c, int64_t k0, float4 (&ra)[
         const int k = f / (T::BN / 4), nq = f % (T::BN / 4);
         const float *p = c.B + (k0 + k) * c.ldb + c.n0 + 4 * nq;
         if (MODE == kVec) rb[r] = *reinterpret_cast<const float4 *>(p);
-        else if (MODE == kScalar) rb[r] = load4_scalar(p);
+        else if (MODE == kVecA || MODE == kScalar) rb[r] = load4_scalar(p);
         else rb[r] = load4_clamped(c.B, c.ldb, k0 + k, c.n0 + 4 * nq, c.K, c.N);
     }
 }
@@ -218,36 +235,37 @@ __device__ __forceinline__ void mfmas(const Frag<T> &fr, f32x16 (&acc)[T::FM][T:
                                                                  acc[i][j], 0, 0, 0);
 }
 
-// The K loop of one block tile.  MODE applies to the full slices; the k tail
-// slice (K not a multiple of BK) always takes edge loads.
+// The K loop over slices s0 .. s0+n-1 of one block tile (n >= 1).  Full
+// slices load in MODE; the slice that runs past K (the last one when K is
+// not a multiple of BK) loads with every index checked.
 template <class T, int MODE>
 __device__ __forceinline__ void k_loop(const Ctx<T> &c, float *lds, int arow, int bcol,
-                                       int kbase, f32x16 (&acc)[T::FM][T::FN]) {
+                                       int kbase, f32x16 (&acc)[T::FM][T::FN], int64_t s0,
+                                       int64_t n) {
     constexpr int BK = T::BK, NR = T::NR, U = T::UNROLL;
-    const int64_t slices = ceil_div(c.K, BK);
-    const int64_t full = c.K / BK;            // slices with no k tail
-    if (slices == 0) return;
+    const int64_t full = c.K / BK - s0;        // slices s0+j, j < full, are full
+    const int64_t limit = full < n ? full : n;
 
     float4 ra[NR][T::A_F4], rb[NR][T::B_F4];
     Frag<T> fr[2];
     auto fetch_any = [&](int64_t j, int set) {
-        if (MODE != kEdge && j < full) fetch<T, MODE>(c, j * BK, ra[set], rb[set]);
-        else fetch<T, kEdge>(c, j * BK, ra[set], rb[set]);
+        if (j < limit) fetch<T, MODE>(c, (s0 + j) * BK, ra[set], rb[set]);
+        else fetch<T, kChecked>(c, (s0 + j) * BK, ra[set], rb[set]);
     };
 
     // Prologue: slices 0 and 1 into LDS (loaded together when there are two
     // register sets), slices 2 .. NR+1 into registers, fragments of slice 0
     // into fr[0].
     fetch_any(0, 0);
-    if (NR >= 2 && slices > 1) fetch_any(1, 1);
+    if (NR >= 2 && n > 1) fetch_any(1, 1);
     stage<T>(lds, 0, c.t, ra[0], rb[0]);
-    if (slices > 1) {
+    if (n > 1) {
         if (NR < 2) fetch_any(1, 0);
         stage<T>(lds, 1, c.t, ra[1 % NR], rb[1 % NR]);
     }
 #pragma unroll
     for (int j = 2; j < NR + 2; ++j)
-        if (j < slices) fetch_any(j, j % NR);
+        if (j < n) fetch_any(j, j % NR);
     __syncthreads();
     read_frags<T>(lds, 0, arow, bcol, kbase, fr[0]);
     __syncthreads();   // buffer 0 is rewritten in iteration 0
@@ -260,48 +278,108 @@ __device__ __forceinline__ void k_loop(const Ctx<T> &c, float *lds, int arow, in
     // MFMAs below the workgroup barrier, which makes them wait for the
     // global loads and LDS stores instead of covering them.)
     auto step = [&](int64_t s, int fp, int rp, bool guarded) {
-        if (!guarded || s + 1 < slices) read_frags<T>(lds, fp ^ 1, arow, bcol, kbase, fr[fp ^ 1]);
+        if (!guarded || s + 1 < n) read_frags<T>(lds, fp ^ 1, arow, bcol, kbase, fr[fp ^ 1]);
         __builtin_amdgcn_sched_barrier(0);
         mfmas<T, 0, T::HALF / 2>(fr[fp], acc);
         __builtin_amdgcn_sched_barrier(0);
-        if (!guarded || s + 2 < slices) {
+        if (!guarded || s + 2 < n) {
             stage<T>(lds, fp, c.t, ra[rp], rb[rp]);
-            if (!guarded) fetch<T, MODE>(c, (s + 2 + NR) * BK, ra[rp], rb[rp]);
-            else if (s + 2 + NR < slices) fetch_any(s + 2 + NR, rp);
+            if (!guarded) fetch<T, MODE>(c, (s0 + s + 2 + NR) * BK, ra[rp], rb[rp]);
+            else if (s + 2 + NR < n) fetch_any(s + 2 + NR, rp);
         }
         __builtin_amdgcn_sched_barrier(0);
         mfmas<T, T::HALF / 2, T::HALF>(fr[fp], acc);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
     };
-    const int64_t limit = MODE != kEdge ? full : slices;   // the main loop fetches below this
     int64_t s = 0;
     for (; s + U - 1 + 2 + NR < limit; s += U) {
 #pragma unroll
         for (int u = 0; u < U; ++u) step(s + u, u & 1, (u + 2) % NR, false);
     }
     // Tail: the last few slices, with checks.  s is a multiple of U here.
-    for (; s < slices; s += U) {
+    for (; s < n; s += U) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (s + u < slices) step(s + u, u & 1, (u + 2) % NR, true);
+            if (s + u < n) step(s + u, u & 1, (u + 2) % NR, true);
     }
 }
 
+// How the work of one launch is cut up.  Logical tiles [0, sk_tiles) --
+// the last partial wave of tiles -- are shared out by K slice
+// ("stream-K"): their tiles x ipt slices are split into sk_wgs contiguous
+// runs, q + 1 slices for the first rm workgroups and q for the rest, so
+// every such workgroup does the same amount of work.  A workgroup that
+// covers a whole tile stores it to C; one that covers part of a tile
+// stores its partial sum to the workspace (slot 2w for the first tile of
+// its run, 2w + 1 for the last), and the fixup adds the partial sums of
+// each such tile in K order.  The remaining tiles [sk_tiles, tiles) are
+// done one per workgroup ("data-parallel").  sk_tiles = 0 is the plain
+// one-tile-per-workgroup launch.
+// Counts that fit 32 bits: tiles (the grid is below 2^31) and stream-K
+// slices (the split is only planned when sk_tiles * ipt < 2^31).
+struct SkPlan {
+    int64_t ipt;        // K slices per tile, ceil(K / BK)
+    float *ws;          // 2 * sk_wgs partial tiles, BM x BN row-major each
+    int tiles_m, tiles_n;
+    int sk_tiles;       // logical tiles done by stream-K workgroups
+    int sk_wgs;         // stream-K workgroups (the first sk_wgs ids)
+    int q, rm;          // slices per stream-K workgroup: q + 1 for w < rm, else q
+};
+
+// First slice (in the stream-K slice order) of stream-K workgroup w.
+__host__ __device__ __forceinline__ int sk_begin(const SkPlan &p, int w) {
+    return w * p.q + (w < p.rm ? w : p.rm);
+}
+
+// Stream-K workgroup that runs slice `it`.
+__host__ __device__ __forceinline__ int sk_owner(const SkPlan &p, int it) {
+    const int big = p.rm * (p.q + 1);
+    return it < big ? it / (p.q + 1) : p.rm + (it - big) / p.q;
+}
+
+// Workspace slot of the partial sum of tile `tile` by stream-K workgroup w.
+__host__ __device__ __forceinline__ int sk_slot(const SkPlan &p, int w, int tile) {
+    return 2 * w + (tile == sk_begin(p, w) / static_cast<int>(p.ipt) ? 0 : 1);
+}
+
+// Where block tile (tm, tn) sits.  A tile that would cross row M (column
+// N) of a matrix at least BM rows (BN columns) large is moved back to end at
+// row M (column N), so every load of a full slice stays inside the
+// matrices with no checks; its first skip_m rows (skip_n columns) belong to
+// the tile before it and are not stored.  Only matrices smaller than a tile
+// leave tiles that hang over an edge (loaded with checks).
+struct Origin {
+    int64_t m0, n0;
+    int skip_m, skip_n;
+};
+
+template <int BM, int BN>
+__host__ __device__ __forceinline__ Origin tile_origin(int64_t tm, int64_t tn, int64_t M,
+                                                       int64_t N) {
+    Origin o{tm * BM, tn * BN, 0, 0};
+    if (o.m0 + BM > M && M >= BM) {
+        o.skip_m = static_cast<int>(o.m0 + BM - M);
+        o.m0 = M - BM;
+    }
+    if (o.n0 + BN > N && N >= BN) {
+        o.skip_n = static_cast<int>(o.n0 + BN - N);
+        o.n0 = N - BN;
+    }
+    return o;
+}
+
+// One pass of the block tile at (c.m0, c.n0) over slices s0 .. s0+n-1
+// (n = 0: a zero tile).  Stores rows [row_lo, rows) and columns
+// [col_lo, cols) of the tile to `out` (its corner, leading dimension ldo).
 template <class T>
-__global__ __launch_bounds__(T::THREADS)
-void gemm_mfma_f32(int64_t M, int64_t N, int64_t K,
-                   const float *__restrict__ A, int64_t lda,
-                   const float *__restrict__ B, int64_t ldb,
-                   float *__restrict__ C, int64_t ldc,
-                   int64_t tiles_m, int64_t tiles_n, int vec_a, int vec_b)
-{
+__device__ __forceinline__ void tile_pass(const Ctx<T> &c, int vec_a, int vec_b, float *lds,
+                                          int64_t s0, int64_t n, float *out, int64_t ldo,
+                                          int row_lo, int64_t rows, int col_lo, int64_t cols) {
     constexpr int BM = T::BM, BN = T::BN, WM = T::WM, WN = T::WN;
     constexpr int FM = T::FM, FN = T::FN, KG = T::KG;
 
-    __shared__ __attribute__((aligned(16))) float lds[T::LDS_WORDS];
-
-    const int t = threadIdx.x;
+    const int t = c.t;
     const int lane = t & 63, wave = t >> 6;
     const int l32 = lane & 31, h = lane >> 5;
     const int grp = wave / T::WAVES;            // K group of this wave
@@ -309,11 +387,6 @@ void gemm_mfma_f32(int64_t M, int64_t N, int64_t K,
     const int wm0 = (wig / T::WAVES_N) * WM;
     const int wn0 = (wig % T::WAVES_N) * WN;
     const int kbase = grp * T::SUB + h * T::HALF;   // this lane's first k in a slice
-
-    int64_t tm, tn;
-    grouped_tile(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, 8, tm, tn);
-    const int64_t m0 = tm * BM, n0 = tn * BN;
-    const Ctx<T> c{M, N, K, A, lda, B, ldb, m0, n0, t};
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -323,13 +396,17 @@ void gemm_mfma_f32(int64_t M, int64_t N, int64_t K,
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const bool whole = (m0 + BM <= M) && (n0 + BN <= N);
-    if (whole && vec_a && vec_b)
-        k_loop<T, kVec>(c, lds, wm0 + l32, wn0 + l32, kbase, acc);
-    else if (whole)
-        k_loop<T, kScalar>(c, lds, wm0 + l32, wn0 + l32, kbase, acc);
-    else
-        k_loop<T, kEdge>(c, lds, wm0 + l32, wn0 + l32, kbase, acc);
+    if (n > 0) {
+        const bool inside = (c.m0 + BM <= c.M) && (c.n0 + BN <= c.N);
+        if (!inside)
+            k_loop<T, kChecked>(c, lds, wm0 + l32, wn0 + l32, kbase, acc, s0, n);
+        else if (vec_a && vec_b && (c.n0 & 3) == 0)
+            k_loop<T, kVec>(c, lds, wm0 + l32, wn0 + l32, kbase, acc, s0, n);
+        else if (vec_a)
+            k_loop<T, kVecA>(c, lds, wm0 + l32, wn0 + l32, kbase, acc, s0, n);
+        else
+            k_loop<T, kScalar>(c, lds, wm0 + l32, wn0 + l32, kbase, acc, s0, n);
+    }
 
     if (KG > 1) {
         // K groups 1..KG-1 hand their partial sums to group 0 through LDS
@@ -365,25 +442,168 @@ void gemm_mfma_f32(int64_t M, int64_t N, int64_t K,
     // Epilogue: word r of accumulator (i, j) is row 8*(r/4) + 4*h + r%4,
     // column l32 of that 32x32 block.  Each store covers two 128-byte row
     // segments per wave.
+    const bool whole = row_lo == 0 && col_lo == 0 && rows >= BM && cols >= BN;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int64_t gn = n0 + wn0 + 32 * j + l32;
+            const int cn = wn0 + 32 * j + l32;
             if (whole) {
-                float *cp = C + (m0 + wm0 + 32 * i + 4 * h) * ldc + gn;
+                float *cp = out + (wm0 + 32 * i + 4 * h) * ldo + cn;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) cp[(8 * (r / 4) + (r % 4)) * ldc] = acc[i][j][r];
+                for (int r = 0; r < 16; ++r) cp[(8 * (r / 4) + (r % 4)) * ldo] = acc[i][j][r];
                 __builtin_amdgcn_sched_barrier(0);   // one block's addresses live at a time
                 continue;
             }
-            if (gn >= N) continue;
+            if (cn < col_lo || cn >= cols) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t gm = m0 + wm0 + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
-                if (gm < M) C[gm * ldc + gn] = acc[i][j][r];
+                const int cm = wm0 + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
+                if (cm >= row_lo && cm < rows) out[cm * ldo + cn] = acc[i][j][r];
             }
         }
+    }
+}
+
+// Float4 chunks of one fixup workgroup: a stream-K tile is finished by
+// BM*BN/4 / THREADS workgroups, one float4 per lane.
+template <class T>
+constexpr int fix_chunks() {
+    return T::BM * T::BN / 4 / T::THREADS;
+}
+
+// Adds the partial sums of one chunk of a stream-K tile in K order (so the
+// result does not depend on which workgroup finished first) and stores it
+// to C.  Tiles that a single stream-K workgroup covered were stored by it.
+template <class T>
+__device__ __forceinline__ void sk_fixup(int job, int64_t M, int64_t N, float *C, int64_t ldc,
+                                         const SkPlan &p, int vec_c) {
+    constexpr int BM = T::BM, BN = T::BN;
+    static_assert(BM * BN / 4 % T::THREADS == 0, "whole fixup chunks");
+    const int tile = job / fix_chunks<T>();
+    const int f = (job % fix_chunks<T>()) * T::THREADS + static_cast<int>(threadIdx.x);
+    const int ipt = static_cast<int>(p.ipt);
+    const int w_lo = sk_owner(p, tile * ipt);
+    const int w_hi = sk_owner(p, (tile + 1) * ipt - 1);
+    if (w_lo == w_hi) return;
+    int64_t tm, tn;
+    grouped_tile(tile, p.tiles_m, p.tiles_n, 8, tm, tn);
+    const Origin o = tile_origin<BM, BN>(tm, tn, M, N);
+    const int row = f / (BN / 4), col = 4 * (f % (BN / 4));
+    const int64_t gm = o.m0 + row, gn = o.n0 + col;
+    if (row < o.skip_m || gm >= M) return;
+    auto part = [&](int w) {
+        return reinterpret_cast<const float4 *>(
+            p.ws + static_cast<int64_t>(sk_slot(p, w, tile)) * (BM * BN))[f];
+    };
+    float4 s = part(w_lo);
+    // the loads of several partial sums are in flight at once; the adds
+    // stay in K order
+#pragma unroll 8
+    for (int w = w_lo + 1; w <= w_hi; ++w) {
+        const float4 v = part(w);
+        s.x += v.x;
+        s.y += v.y;
+        s.z += v.z;
+        s.w += v.w;
+    }
+    float *cp = C + gm * ldc + gn;
+    if (vec_c && col >= o.skip_n && (gn & 3) == 0 && gn + 3 < N) {
+        *reinterpret_cast<float4 *>(cp) = s;
+    } else {
+        const float e[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (col + q >= o.skip_n && gn + q < N) cp[q] = e[q];
+    }
+}
+
+// The main launch: workgroups [0, sk_tiles * fix_chunks) finish the
+// stream-K tiles (the stream-K launch has completed before this one
+// starts), the rest run one data-parallel tile each.  Without a split
+// (sk_tiles = 0) every workgroup runs one tile.
+template <class T>
+__global__ __launch_bounds__(T::THREADS)
+void gemm_mfma_f32(int64_t M, int64_t N, int64_t K,
+                   const float *__restrict__ A, int64_t lda,
+                   const float *__restrict__ B, int64_t ldb,
+                   float *__restrict__ C, int64_t ldc, SkPlan p, int vec_a, int vec_b,
+                   int vec_c)
+{
+    __shared__ __attribute__((aligned(16))) float lds[T::LDS_WORDS];
+
+    const int bid = static_cast<int>(blockIdx.x);
+    const int fix = p.sk_tiles * fix_chunks<T>();
+    if (bid < fix) {
+        sk_fixup<T>(bid, M, N, C, ldc, p, vec_c);
+        return;
+    }
+    const int dp = p.tiles_m * p.tiles_n - p.sk_tiles;
+    const int tile = p.sk_tiles + static_cast<int>(xcd_remap(bid - fix, dp));
+    int64_t tm, tn;
+    grouped_tile(tile, p.tiles_m, p.tiles_n, 8, tm, tn);
+    const Origin o = tile_origin<T::BM, T::BN>(tm, tn, M, N);
+    const Ctx<T> c{M, N, K, A, lda, B, ldb, o.m0, o.n0, static_cast<int>(threadIdx.x)};
+    const int64_t rows = M - o.m0 < T::BM ? M - o.m0 : T::BM;
+    const int64_t cols = N - o.n0 < T::BN ? N - o.n0 : T::BN;
+    tile_pass<T>(c, vec_a, vec_b, lds, 0, p.ipt, C + o.m0 * ldc + o.n0, ldc, o.skip_m, rows,
+                 o.skip_n, cols);
+}
+
+// The stream-K launch: workgroup w runs slices [sk_begin(w), sk_begin(w+1))
+// of the stream-K tiles in order, one segment per tile it touches.  A
+// segment that covers a whole tile is stored to C; a partial one to the
+// workspace slot of (w, tile).
+template <class T>
+__global__ __launch_bounds__(T::THREADS) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm_mfma_f32_sk(int64_t M, int64_t N, int64_t K,
+                      const float *__restrict__ A, int64_t lda,
+                      const float *__restrict__ B, int64_t ldb,
+                      float *__restrict__ C, int64_t ldc, SkPlan p, int vec_a, int vec_b)
+{
+    __shared__ __attribute__((aligned(16))) float lds[T::LDS_WORDS];
+
+    const int ipt = static_cast<int>(p.ipt);
+    const int w = static_cast<int>(xcd_remap(blockIdx.x, p.sk_wgs));
+    const int end = sk_begin(p, w + 1);
+    int it = sk_begin(p, w);
+    Ctx<T> c{M, N, K, A, lda, B, ldb, 0, 0, 0};
+    for (;;) {
+        const int tile = it / ipt, kb = it - tile * ipt;
+        const int ke = ipt < kb + (end - it) ? ipt : kb + (end - it);
+        int64_t tm, tn;
+        grouped_tile(tile, p.tiles_m, p.tiles_n, 8, tm, tn);
+        const Origin o = tile_origin<T::BM, T::BN>(tm, tn, M, N);
+        c.m0 = o.m0;
+        c.n0 = o.n0;
+        float *out;
+        int64_t ldo, rows, cols;
+        int row_lo, col_lo;
+        if (kb == 0 && ke == ipt) {            // the whole K range: final values
+            out = C + o.m0 * ldc + o.n0;
+            ldo = ldc;
+            row_lo = o.skip_m;
+            col_lo = o.skip_n;
+            rows = M - o.m0 < T::BM ? M - o.m0 : T::BM;
+            cols = N - o.n0 < T::BN ? N - o.n0 : T::BN;
+        } else {                                // part of it: a partial sum
+            out = p.ws + static_cast<int64_t>(sk_slot(p, w, tile)) * (T::BM * T::BN);
+            ldo = T::BN;
+            row_lo = col_lo = 0;
+            rows = T::BM;
+            cols = T::BN;
+        }
+        // The lane id and the operands are laundered per segment: otherwise
+        // the compiler hoists the addresses of all four load modes out of
+        // the segment loop and keeps them live at once (spilling).
+        int lane_id = static_cast<int>(threadIdx.x);
+        asm volatile("" : "+v"(lane_id));
+        c.t = lane_id;
+        asm volatile("" : "+s"(c.A), "+s"(c.B), "+s"(c.lda), "+s"(c.ldb));
+        tile_pass<T>(c, vec_a, vec_b, lds, kb, ke - kb, out, ldo, row_lo, rows, col_lo, cols);
+        it += ke - kb;
+        if (it >= end) break;
+        __syncthreads();   // LDS is reused by the next segment
     }
 }
 
@@ -399,57 +619,178 @@ using TileLarge = MfmaTile<128, 128, 16, 64, 64, 1, 2>;
 using TileMany = MfmaTile<64, 64, 32, 32, 32, 1, 2>;
 using TileFew = MfmaTile<64, 64, 64, 32, 64, 4, 1>;
 
-constexpr int64_t kCUs = 256;
+constexpr int64_t kMi355xCUs = 256;
 
 enum class Shape { kLarge, kMany, kFew };
 
 Shape pick(int64_t M, int64_t N, int64_t K) {
     const int64_t large_tiles = ceil_div(M, TileLarge::BM) * ceil_div(N, TileLarge::BN);
-    if (large_tiles >= 4 * kCUs) return Shape::kLarge;
+    if (large_tiles >= 4 * kMi355xCUs) return Shape::kLarge;
     const int64_t small_tiles = ceil_div(M, TileMany::BM) * ceil_div(N, TileMany::BN);
-    if (small_tiles > 2 * kCUs && K < 4096) return Shape::kMany;
+    if (small_tiles > 2 * kMi355xCUs && K < 4096) return Shape::kMany;
     return Shape::kFew;
 }
 
+// Compute units of the current device (MI355X's 256 if it cannot be read).
+int64_t device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kMi355xCUs;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0) {
+        (void)hipGetLastError();
+        return kMi355xCUs;
+    }
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Workgroups of the stream-K kernel resident per CU (`fallback`, the value
+// measured on gfx950, if the runtime cannot say).
 template <class T>
-LaunchPlan plan_for(int64_t M, int64_t N, const char *name) {
+int64_t resident_per_cu(int fallback) {
+    static std::atomic<int> cache{0};
+    int n = cache.load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_mfma_f32_sk<T>, T::THREADS, 0) !=
+            hipSuccess ||
+        n <= 0) {
+        (void)hipGetLastError();
+        return fallback;
+    }
+    cache.store(n, std::memory_order_relaxed);
+    return n;
+}
+
+template <class T>
+int resident_fallback() {
+    return T::KG > 1 ? 1 : 2;   // measured on gfx950 for the three tile classes
+}
+
+// The work split of a launch.  Without stream-K, or when the tiles fill
+// whole waves of resident workgroups, every tile is data-parallel.
+// Otherwise the tiles of the last partial wave (all tiles if there are
+// fewer than one wave) are shared out by slice over up to one wave of
+// workgroups, each with at least 2 slices and at least an eighth of a
+// tile's slices, so a tile has at most about 8 partial sums to add.
+template <class T>
+SkPlan plan_split(int64_t M, int64_t N, int64_t K, bool stream_k) {
+    SkPlan p{};
+    const int64_t tiles_m = ceil_div(M, T::BM), tiles_n = ceil_div(N, T::BN);
+    const int64_t tiles = tiles_m * tiles_n;
+    p.ipt = ceil_div(K, T::BK);
+    if (tiles > kMaxGrid) return p;   // rejected before launch
+    p.tiles_m = static_cast<int>(tiles_m);
+    p.tiles_n = static_cast<int>(tiles_n);
+    if (!stream_k || p.ipt < 2) return p;
+    const int64_t slots = device_cus() * resident_per_cu<T>(resident_fallback<T>());
+    if (tiles % slots == 0) return p;
+    const int64_t sk_tiles = tiles % slots;
+    const int64_t total = sk_tiles * p.ipt;
+    if (total > kMaxGrid) return p;   // slice counts must fit 32 bits
+    const int64_t min_slices = std::max<int64_t>(2, ceil_div(p.ipt, 8));
+    const int64_t sk_wgs = std::max<int64_t>(1, std::min(slots, total / min_slices));
+    p.sk_tiles = static_cast<int>(sk_tiles);
+    p.sk_wgs = static_cast<int>(sk_wgs);
+    p.q = static_cast<int>(total / sk_wgs);
+    p.rm = static_cast<int>(total % sk_wgs);
+    return p;
+}
+
+template <class T>
+size_t workspace_bytes(const SkPlan &p) {
+    return static_cast<size_t>(2 * p.sk_wgs) * T::BM * T::BN * sizeof(float);
+}
+
+template <class T>
+LaunchPlan plan_for(int64_t M, int64_t N, int64_t K, bool stream_k, const char *name) {
+    const SkPlan s = plan_split<T>(M, N, K, stream_k);
     LaunchPlan p{};
     p.kernel = name;
     p.bm = T::BM;
     p.bn = T::BN;
     p.bk = T::BK;
-    p.grid = ceil_div(M, T::BM) * ceil_div(N, T::BN);
+    p.grid = ceil_div(M, T::BM) * ceil_div(N, T::BN) +
+             static_cast<int64_t>(s.sk_tiles) * (fix_chunks<T>() - 1);   // the main launch
     p.block = T::THREADS;
     p.lds_bytes = static_cast<int>(T::LDS_WORDS * sizeof(float));
     p.split_k = 1;
+    p.sk_tiles = s.sk_tiles;
+    p.sk_wgs = s.sk_wgs;
+    p.workspace_bytes = workspace_bytes<T>(s);
     return p;
 }
 
 template <class T>
-hipError_t launch_tile(const GemmArgs &a) {
-    const int64_t tm = ceil_div(a.M, T::BM), tn = ceil_div(a.N, T::BN);
-    hipLaunchKernelGGL(gemm_mfma_f32<T>, dim3(static_cast<uint32_t>(tm * tn)), dim3(T::THREADS),
-                       0, a.stream, a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, tm, tn,
-                       static_cast<int>(vec4_ok(a.A, a.lda)),
-                       static_cast<int>(vec4_ok(a.B, a.ldb)));
+hipError_t launch_tile(const GemmArgs &a, bool stream_k, void *ws, size_t ws_bytes) {
+    SkPlan p = plan_split<T>(a.M, a.N, a.K, stream_k);
+    if (workspace_bytes<T>(p) > ws_bytes || (p.sk_wgs > 0 && ws == nullptr))
+        return hipErrorInvalidValue;
+    p.ws = static_cast<float *>(ws);
+    const int vec_a = vec4_ok(a.A, a.lda), vec_b = vec4_ok(a.B, a.ldb);
+    if (p.sk_wgs > 0) {
+        hipLaunchKernelGGL(gemm_mfma_f32_sk<T>, dim3(static_cast<uint32_t>(p.sk_wgs)),
+                           dim3(T::THREADS), 0, a.stream, a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb,
+                           a.C, a.ldc, p, vec_a, vec_b);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    // fixups of the stream-K tiles, then the data-parallel tiles
+    const int64_t grid = static_cast<int64_t>(p.tiles_m) * p.tiles_n +
+                         static_cast<int64_t>(p.sk_tiles) * (fix_chunks<T>() - 1);
+    hipLaunchKernelGGL(gemm_mfma_f32<T>, dim3(static_cast<uint32_t>(grid)), dim3(T::THREADS), 0,
+                       a.stream, a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, p, vec_a,
+                       vec_b, static_cast<int>(vec4_ok(a.C, a.ldc)));
     return hipGetLastError();
 }
 
 }  // namespace
 
-LaunchPlan plan_mfma(int64_t M, int64_t N, int64_t K) {
+LaunchPlan plan_mfma(int64_t M, int64_t N, int64_t K, bool stream_k) {
     switch (pick(M, N, K)) {
-        case Shape::kLarge: return plan_for<TileLarge>(M, N, "gemm_mfma_f32<128x128x16, 4 waves>");
-        case Shape::kMany: return plan_for<TileMany>(M, N, "gemm_mfma_f32<64x64x32, 4 waves>");
-        default: return plan_for<TileFew>(M, N, "gemm_mfma_f32<64x64x64, 4 K groups>");
+        case Shape::kLarge:
+            return plan_for<TileLarge>(M, N, K, stream_k, "gemm_mfma_f32<128x128x16, 4 waves>");
+        case Shape::kMany:
+            return plan_for<TileMany>(M, N, K, stream_k, "gemm_mfma_f32<64x64x32, 4 waves>");
+        default:
+            return plan_for<TileFew>(M, N, K, stream_k, "gemm_mfma_f32<64x64x64, 4 K groups>");
     }
 }
 
-hipError_t launch_mfma(const GemmArgs &a) {
+// AUTO's choice, from timings of both forms on MI355X: the stream-K split
+// pays when one tile per workgroup would leave some CUs a whole tile more
+// work than the mean (at least 10% more: e.g. 1296 tiles on 256 CUs, 5.06 a
+// CU, so some CUs run 6), K has at least 8 slices to share out, and the
+// product is large enough (>= 4 GFLOP) to hide the second launch.  Shapes
+// that split evenly over the CUs, like 2304 tiles on 256, stay
+// data-parallel.
+template <class T>
+bool stream_k_pays(int64_t M, int64_t N, int64_t K) {
+    const SkPlan p = plan_split<T>(M, N, K, true);
+    if (p.sk_tiles == 0 || p.ipt < 8) return false;
+    if (2.0 * static_cast<double>(M) * static_cast<double>(N) * static_cast<double>(K) < 4e9)
+        return false;
+    const int64_t cus = device_cus();
+    const int64_t tiles = static_cast<int64_t>(p.tiles_m) * p.tiles_n;
+    const int64_t per_cu = ceil_div(tiles, cus);
+    return static_cast<double>(per_cu * cus) >= 1.1 * static_cast<double>(tiles);
+}
+
+bool prefer_stream_k(int64_t M, int64_t N, int64_t K) {
+    switch (pick(M, N, K)) {
+        case Shape::kLarge: return stream_k_pays<TileLarge>(M, N, K);
+        case Shape::kMany: return stream_k_pays<TileMany>(M, N, K);
+        default: return stream_k_pays<TileFew>(M, N, K);
+    }
+}
+
+hipError_t launch_mfma(const GemmArgs &a, bool stream_k, void *ws, size_t ws_bytes) {
     switch (pick(a.M, a.N, a.K)) {
-        case Shape::kLarge: return launch_tile<TileLarge>(a);
-        case Shape::kMany: return launch_tile<TileMany>(a);
-        default: return launch_tile<TileFew>(a);
+        case Shape::kLarge: return launch_tile<TileLarge>(a, stream_k, ws, ws_bytes);
+        case Shape::kMany: return launch_tile<TileMany>(a, stream_k, ws, ws_bytes);
+        default: return launch_tile<TileFew>(a, stream_k, ws, ws_bytes);
     }
 }
 

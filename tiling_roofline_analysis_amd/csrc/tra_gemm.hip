@@ -15,6 +15,8 @@
 
 #include <cstdio>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "gemm_internal.h"
 
@@ -45,16 +47,83 @@ bool overlaps(const Extent &a, const Extent &b) { return a.lo < b.hi && b.lo < a
 
 bool valid_variant(int v) { return v >= TRA_GEMM_AUTO && v < TRA_GEMM_VARIANT_COUNT; }
 
+// The rung AUTO runs for a shape.
+int resolve(int variant, int64_t M, int64_t N, int64_t K) {
+    if (variant != TRA_GEMM_AUTO) return variant;
+    return tra::prefer_stream_k(M, N, K) ? TRA_GEMM_MFMA_STREAMK : TRA_GEMM_MFMA;
+}
+
 tra::LaunchPlan plan_of(int variant, int64_t M, int64_t N, int64_t K) {
-    switch (variant) {
+    switch (resolve(variant, M, N, K)) {
         case TRA_GEMM_NAIVE: return tra::plan_naive(M, N, K);
         case TRA_GEMM_LDS_TILED: return tra::plan_lds_tiled(M, N, K);
         case TRA_GEMM_REGBLOCK_DB: return tra::plan_regblock(M, N, K);
-        default: return tra::plan_mfma(M, N, K);   // AUTO and MFMA
+        case TRA_GEMM_MFMA_STREAMK: return tra::plan_mfma(M, N, K, true);
+        default: return tra::plan_mfma(M, N, K, false);
     }
 }
 
-// Host-side checks only; touches no device.  On success M, N > 0.
+// The library's own workspaces, one per (device, stream) pair.  Work on one
+// stream runs in order, so calls on that stream may share one buffer; a
+// buffer is only replaced (by a larger one) after its stream has drained.
+// The mutex is held from the lookup until the kernels are enqueued, so a
+// replacement cannot free a buffer another thread is about to launch with.
+struct LibWorkspace {
+    int device;
+    hipStream_t stream;
+    void *ptr;
+    size_t bytes;
+};
+std::mutex g_ws_mutex;
+std::vector<LibWorkspace> g_ws;
+
+// Finds or grows the workspace of (current device, stream); caller holds
+// g_ws_mutex.
+hipError_t library_workspace(hipStream_t stream, size_t bytes, void **out) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    for (LibWorkspace &w : g_ws) {
+        if (w.device != dev || w.stream != stream) continue;
+        if (w.bytes >= bytes) {
+            *out = w.ptr;
+            return hipSuccess;
+        }
+        if ((err = hipStreamSynchronize(stream)) != hipSuccess) return err;
+        if ((err = hipFree(w.ptr)) != hipSuccess) return err;
+        w.ptr = nullptr;
+        w.bytes = 0;
+        const size_t grown = (bytes + (1u << 20) - 1) & ~static_cast<size_t>((1u << 20) - 1);
+        if ((err = hipMalloc(&w.ptr, grown)) != hipSuccess) return err;
+        w.bytes = grown;
+        *out = w.ptr;
+        return hipSuccess;
+    }
+    const size_t grown = (bytes + (1u << 20) - 1) & ~static_cast<size_t>((1u << 20) - 1);
+    void *p = nullptr;
+    if ((err = hipMalloc(&p, grown)) != hipSuccess) return err;
+    g_ws.push_back(LibWorkspace{dev, stream, p, grown});
+    *out = p;
+    return hipSuccess;
+}
+
+hipError_t launch(int variant, const tra::GemmArgs &a, void *ws, size_t ws_bytes) {
+    switch (variant) {
+        case TRA_GEMM_NAIVE: return tra::launch_naive(a);
+        case TRA_GEMM_LDS_TILED: return tra::launch_lds_tiled(a);
+        case TRA_GEMM_REGBLOCK_DB: return tra::launch_regblock(a);
+        case TRA_GEMM_MFMA_STREAMK: return tra::launch_mfma(a, true, ws, ws_bytes);
+        default: return tra::launch_mfma(a, false, ws, ws_bytes);
+    }
+}
+
+tra_status hip_status(hipError_t err) {
+    if (err == hipSuccess) return TRA_OK;
+    tra::record_hip_error(err);
+    return TRA_ERR_HIP;
+}
+
+// Host-side checks; launches nothing.  On success M, N > 0.
 tra_status check_args(int variant, int64_t M, int64_t N, int64_t K, const float *A,
                       int64_t lda, const float *B, int64_t ldb, const float *C, int64_t ldc,
                       bool &noop) {
@@ -93,18 +162,38 @@ tra_status gemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K, const 
     const tra_status st = check_args(variant, M, N, K, A, lda, B, ldb, C, ldc, noop);
     if (st != TRA_OK || noop) return st;
 
-    tra::GemmArgs a{M, N, K, A, lda, B, ldb, C, ldc, static_cast<hipStream_t>(stream)};
-    hipError_t err;
-    switch (variant) {
-        case TRA_GEMM_NAIVE: err = tra::launch_naive(a); break;
-        case TRA_GEMM_LDS_TILED: err = tra::launch_lds_tiled(a); break;
-        case TRA_GEMM_REGBLOCK_DB: err = tra::launch_regblock(a); break;
-        default: err = tra::launch_mfma(a); break;   // AUTO and MFMA
-    }
-    if (err != hipSuccess) {
-        tra::record_hip_error(err);
-        return TRA_ERR_HIP;
-    }
+    const int v = resolve(variant, M, N, K);
+    const tra::GemmArgs a{M, N, K, A, lda, B, ldb, C, ldc, static_cast<hipStream_t>(stream)};
+    const size_t need = plan_of(v, M, N, K).workspace_bytes;
+    if (need == 0) return hip_status(launch(v, a, nullptr, 0));
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    void *ws = nullptr;
+    const hipError_t err = library_workspace(a.stream, need, &ws);
+    if (err != hipSuccess) return hip_status(err);
+    return hip_status(launch(v, a, ws, need));
+}
+
+tra_status gemm_f32_variant_ws(int variant, int64_t M, int64_t N, int64_t K, const float *A,
+                               int64_t lda, const float *B, int64_t ldb, float *C, int64_t ldc,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+    bool noop = false;
+    const tra_status st = check_args(variant, M, N, K, A, lda, B, ldb, C, ldc, noop);
+    if (st != TRA_OK || noop) return st;
+
+    const int v = resolve(variant, M, N, K);
+    const size_t need = plan_of(v, M, N, K).workspace_bytes;
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need ||
+                     (reinterpret_cast<uintptr_t>(workspace) & 15u) != 0))
+        return TRA_ERR_INVALID_ARG;
+    const tra::GemmArgs a{M, N, K, A, lda, B, ldb, C, ldc, static_cast<hipStream_t>(stream)};
+    return hip_status(launch(v, a, workspace, workspace_bytes));
+}
+
+tra_status tra_gemm_workspace_size(int variant, int64_t M, int64_t N, int64_t K,
+                                   size_t *bytes) {
+    if (!valid_variant(variant) || M < 0 || N < 0 || K < 0 || bytes == nullptr)
+        return TRA_ERR_INVALID_ARG;
+    *bytes = (M == 0 || N == 0) ? 0 : plan_of(variant, M, N, K).workspace_bytes;
     return TRA_OK;
 }
 
@@ -120,9 +209,13 @@ tra_status tra_gemm_describe(int variant, int64_t M, int64_t N, int64_t K, char 
     if (len == 0) return TRA_OK;
     const tra::LaunchPlan p = plan_of(variant, M, N, K);
     std::snprintf(buf, len,
-                  "variant=%s kernel=%s tile=%dx%dx%d grid=%lld block=%d lds_bytes=%d split_k=%d",
-                  tra_gemm_variant_name(variant), p.kernel, p.bm, p.bn, p.bk,
-                  static_cast<long long>(p.grid), p.block, p.lds_bytes, p.split_k);
+                  "variant=%s rung=%s kernel=%s tile=%dx%dx%d grid=%lld block=%d lds_bytes=%d "
+                  "split_k=%d stream_k_tiles=%lld stream_k_wgs=%lld workspace_bytes=%zu",
+                  tra_gemm_variant_name(variant),
+                  tra_gemm_variant_name(resolve(variant, M, N, K)), p.kernel, p.bm, p.bn, p.bk,
+                  static_cast<long long>(p.grid), p.block, p.lds_bytes, p.split_k,
+                  static_cast<long long>(p.sk_tiles), static_cast<long long>(p.sk_wgs),
+                  p.workspace_bytes);
     return TRA_OK;
 }
 
@@ -143,6 +236,7 @@ const char *tra_gemm_variant_name(int variant) {
         case TRA_GEMM_LDS_TILED: return "lds_tiled";
         case TRA_GEMM_REGBLOCK_DB: return "regblock_db";
         case TRA_GEMM_MFMA: return "mfma";
+        case TRA_GEMM_MFMA_STREAMK: return "mfma_streamk";
         default: return "unknown";
     }
 }

@@ -21,6 +21,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import os
 import sqlite3
 import sys
@@ -34,12 +35,21 @@ COPY_BYTES = 64 << 22    # 64 Mi floats = 256 MiB read and 256 MiB written
 COPY_KERNEL = "copyBuffer"
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments and blank space removed (string literals
+    with comment markers do not occur in these files)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest(files=("gemm_mfma.hip", "gemm_internal.h")) -> str:
-    """Short sha256 of the MFMA rung's HIP sources."""
+    """Short sha256 of the code (comments and spacing aside) of the MFMA
+    rung's HIP sources: a counter reading is current while this matches."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(HERE, "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(HERE, "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
