@@ -112,6 +112,78 @@ def measure_roofs(tra, torch):
     return out
 
 
+def host_inclusive(tra, torch, w, reps=5):
+    """Host-to-host time of one product, as page "[AutoMine++] #2 matmul
+    trial and error" timed its SYCL routine (section "Implementing with SYCL
+    (iGPU) + performance comparison"): device buffers, host-to-device copies
+    of A and B, the GEMM, the copy of C back, all inside the clock.  Device buffers come
+    from torch's caching allocator (cached after the first rep, which is
+    not timed).  Pageable and pinned host memory are both timed."""
+    A, B = w.make()
+    out = {}
+    for mode in ("pageable", "pinned"):
+        hA, hB = torch.from_numpy(A), torch.from_numpy(B)
+        hC = torch.empty((w.M, w.N), dtype=torch.float32)
+        if mode == "pinned":
+            hA, hB, hC = hA.pin_memory(), hB.pin_memory(), hC.pin_memory()
+        times = []
+        for r in range(reps + 1):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            dA = hA.to("cuda:0", non_blocking=(mode == "pinned"))
+            dB = hB.to("cuda:0", non_blocking=(mode == "pinned"))
+            dC = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda:0")
+            tra.matmul(dA, dB, dC)
+            hC.copy_(dC, non_blocking=(mode == "pinned"))
+            torch.cuda.synchronize()
+            if r > 0:
+                times.append(time.perf_counter() - t0)
+            del dA, dB, dC
+        t = statistics.median(times)
+        out[f"{mode}_ms"] = round(t * 1e3, 4)
+        out[f"{mode}_tflops"] = round(w.flops / t / 1e12, 3)
+    out["bytes_over_pcie"] = 4 * (w.M * w.K + w.K * w.N + w.M * w.N)
+    return out
+
+
+def torch_matmul(torch, w, steps):
+    """torch.matmul in strict FP32 (ROCm's vendor GEMM) on the same device-
+    resident inputs, timed like the library: context, not the product."""
+    torch.backends.cuda.matmul.allow_tf32 = False
+    A, B = w.make()
+    dA = torch.from_numpy(A).to("cuda:0")
+    dB = torch.from_numpy(B).to("cuda:0")
+    dC = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    for _ in range(5):
+        torch.matmul(dA, dB, out=dC)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        torch.matmul(dA, dB, out=dC)
+    e1.record(stream)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"ms": round(ms, 5), "tflops": round(w.flops / ms / 1e9, 3)}
+
+
+def numpy_matmul(w):
+    """numpy's float32 matmul (the host BLAS) on the same inputs: the
+    comparison page "[AutoMine++] #2 matmul trial and error" plans in its
+    section "Wrap-up"."""
+    import numpy as np
+    A, B = w.make()
+    np.matmul(A, B)
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        np.matmul(A, B)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"ms": round(t * 1e3, 3), "tflops": round(w.flops / t / 1e12, 4)}
+
+
 def cpu_baseline(w):
     """The CPU oracle on the full headline product, on the host's cores."""
     import oracle
@@ -141,6 +213,10 @@ def main():
     ap.add_argument("--no-roofs", action="store_true", help="skip the roof probes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy 5 times (scales HBM counters)")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip host-inclusive timing and the torch / numpy comparisons")
+    ap.add_argument("--plot", metavar="SVG", help="write the roofline chart of the ladder here")
+    ap.add_argument("--plot-table", metavar="MD", help="write the chart's points as a table here")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -153,7 +229,8 @@ def main():
     import tiling_roofline_analysis_amd as tra
     from tiling_roofline_analysis_amd import inputs
     from tiling_roofline_analysis_amd import roofline as rl
-    from tiling_roofline_analysis_amd.profiling import source_digest, stored_traffic
+    from tiling_roofline_analysis_amd.profiling import (source_digest, stored_ladder_traffic,
+                                                        stored_traffic)
 
     if not os.path.exists(tra.LIB_PATH):
         import __graft_entry__
@@ -249,7 +326,8 @@ def main():
             "ai_flop_per_byte": round(prim["rep"]["ai"], 2),
             "algorithmic_bytes": prim["rep"]["bytes"],
             "source_digest": source_digest(), "gpu_wall_s": round(gpu_wall, 2),
-            "device": torch.cuda.get_device_name(0),
+            "device": (f"{torch.cuda.get_device_name(0)} "
+                       f"({torch.cuda.get_device_properties(0).gcnArchName.split(':')[0]})"),
             "measured_roofs": roofs,
         },
     }
@@ -266,6 +344,20 @@ def main():
         }
         if sec["ladder"]:
             line.setdefault("ladder", {})[SECONDARY] = sec["ladder"]
+    if not args.no_compare:
+        comp = {}
+        for name in (PRIMARY,) + (() if args.no_secondary else (SECONDARY,)):
+            wc = inputs.WORKLOADS[name]
+            comp[name] = {"host_inclusive": host_inclusive(tra, torch, wc),
+                          "torch_matmul_fp32": torch_matmul(torch, wc, args.steps)}
+            log(f"[{name}] host-inclusive {comp[name]['host_inclusive']}; "
+                f"torch.matmul {comp[name]['torch_matmul_fp32']}")
+            torch.cuda.empty_cache()
+        comp[PRIMARY]["numpy_matmul_fp32"] = numpy_matmul(inputs.WORKLOADS[PRIMARY])
+        log(f"[{PRIMARY}] numpy {comp[PRIMARY]['numpy_matmul_fp32']}")
+        line["detail"]["compare"] = comp
+    if args.plot or args.plot_table:
+        rl.write_chart(line, stored_ladder_traffic(), args.plot, args.plot_table)
     if not args.no_cpu_baseline:
         log("[cpu_baseline] timing the oracle ...")
         line["cpu_baseline"] = cpu_baseline(inputs.WORKLOADS[PRIMARY])

@@ -8,7 +8,9 @@ This module turns one into the short text summaries kept under profiles/:
   traffic  HBM bytes per launch of one GEMM kernel from two `--pmc` runs
            (FETCH_SIZE, then WRITE_SIZE, both in KiB per dispatch), each
            scaled by what the same counter reads for a plain device copy of
-           known size in the same run (`bench.py --copy-calibration`).
+           known size in the same run (`bench.py --copy-calibration`);
+  ladder   the same for every rung of the ladder at both configured shapes
+           (bench.py run with its ladder), the points of the roofline chart.
 
 The traffic summary records a digest of the kernel sources; bench.py reports
 the stored traffic only while that digest matches the current sources.
@@ -144,6 +146,99 @@ def traffic_summary(fetch_db, write_db, match, grid, workload, cmd, algorithmic_
     return "\n".join(lines) + "\n"
 
 
+def ladder_traffic(fetch_db, write_db):
+    """Calibrated HBM bytes per launch of every rung of the ladder in two
+    `--pmc` runs of bench.py with its ladder, keyed by (rung, workload).
+    A rung's launch is recognised by its kernel name and its grid, which
+    tra_gemm_describe gives for each configured shape."""
+    sys.path.insert(0, ROOT)
+    import tiling_roofline_analysis_amd as tra
+    from tiling_roofline_analysis_amd import inputs
+
+    def rows(db):
+        c = _db(db)
+        return c.execute(
+            "select kernel_name, grid_size, avg(value), count(*) from counters_collection "
+            "group by kernel_name, grid_size").fetchall()
+
+    out = {}
+    fr, wr = rows(fetch_db), rows(write_db)
+    cf = max((r for r in fr if COPY_KERNEL in r[0]), key=lambda r: r[1])
+    cw = max((r for r in wr if COPY_KERNEL in r[0]), key=lambda r: r[1])
+    fscale, wscale = COPY_BYTES / (cf[2] * 1024.0), COPY_BYTES / (cw[2] * 1024.0)
+    for wname in ("uniform1024", "normal4096"):
+        w = inputs.WORKLOADS[wname]
+        for v in tra.LADDER:
+            d = tra.tra_gemm_describe(v, w.M, w.N, w.K)
+            kv = dict(x.split("=", 1) for x in d.split() if "=" in x)
+            kernel = kv["kernel"].split("<")[0]
+            lanes = int(kv["grid"]) * int(kv["block"])
+            f = [r for r in fr if kernel + "<" in r[0] or kernel + "(" in r[0]]
+            f = [r for r in f if r[1] == lanes]
+            wrow = [r for r in wr if (kernel + "<" in r[0] or kernel + "(" in r[0]) and r[1] == lanes]
+            if len(f) != 1 or len(wrow) != 1:
+                continue
+            out[(tra.tra_gemm_variant_name(v), wname)] = {
+                "kernel": kernel, "lanes": lanes, "dispatches": f[0][3],
+                "read_bytes": f[0][2] * 1024.0 * fscale, "write_bytes": wrow[0][2] * 1024.0 * wscale}
+    return out, fscale, wscale
+
+
+def ladder_summary(fetch_db, write_db, cmd):
+    from tiling_roofline_analysis_amd import inputs, roofline
+    data, fscale, wscale = ladder_traffic(fetch_db, write_db)
+    lines = [
+        "# HBM traffic per launch of each rung (rocprofv3 counters)", "",
+        f"FETCH_SIZE pass: `{cmd.format(counter='FETCH_SIZE')}`", "",
+        f"WRITE_SIZE pass: `{cmd.format(counter='WRITE_SIZE')}`", "",
+        f"Calibration by a plain device copy of {COPY_BYTES} bytes in the same runs: "
+        f"FETCH_SIZE x {fscale:.4f}, WRITE_SIZE x {wscale:.4f}.", "",
+        "| rung | workload | kernel | HBM read B | HBM write B | x algorithmic | achieved AI (flop/B) |",
+        "|---|---|---|---|---|---|---|"]
+    for (rung, wname), d in data.items():
+        w = inputs.WORKLOADS[wname]
+        alg = roofline.gemm_bytes(w.M, w.N, w.K)
+        tot = d["read_bytes"] + d["write_bytes"]
+        lines.append(f"| {rung} | {wname} | {d['kernel']} | {d['read_bytes']:.4g} | "
+                     f"{d['write_bytes']:.4g} | {tot / alg:.2f} | "
+                     f"{roofline.gemm_flops(w.M, w.N, w.K) / tot:.4g} |")
+    lines += ["", f"sources_digest = {all_sources_digest()}"]
+    return "\n".join(lines) + "\n"
+
+
+def all_sources_digest() -> str:
+    """Digest of the code of every kernel source of the library."""
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(HERE, "csrc"))):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(HERE, "csrc", f), encoding="utf-8") as fh:
+                h.update(_code_only(fh.read()).encode())
+    return h.hexdigest()[:16]
+
+
+LADDER_TRAFFIC = os.path.join(PROFILES, "traffic_ladder.md")
+
+
+def stored_ladder_traffic():
+    """{(rung, workload): HBM bytes per launch} from profiles/traffic_ladder.md,
+    or {} when it is absent or the kernel sources changed since."""
+    if not os.path.exists(LADDER_TRAFFIC):
+        return {}
+    text = open(LADDER_TRAFFIC).read()
+    m = re.search(r"sources_digest = (\w+)", text)
+    if not m or m.group(1) != all_sources_digest():
+        return {}
+    out = {}
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 7 and cells[0] not in ("rung", "---"):
+            try:
+                out[(cells[0], cells[1])] = float(cells[3]) + float(cells[4])
+            except ValueError:
+                pass
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description="summarise rocprofv3 results")
     sub = ap.add_subparsers(dest="what", required=True)
@@ -157,9 +252,16 @@ def main(argv=None):
     f.add_argument("--grid", type=int, default=None)
     f.add_argument("--workload", required=True)
     f.add_argument("--cmd", required=True, help="profiling command with {counter}")
+    lad = sub.add_parser("ladder")
+    lad.add_argument("fetch_db")
+    lad.add_argument("write_db")
+    lad.add_argument("--cmd", required=True, help="profiling command with {counter}")
     args = ap.parse_args(argv)
     if args.what == "trace":
         sys.stdout.write(trace_summary(args.db, args.cmd))
+    elif args.what == "ladder":
+        sys.path.insert(0, ROOT)
+        sys.stdout.write(ladder_summary(args.fetch_db, args.write_db, args.cmd))
     else:
         sys.path.insert(0, ROOT)
         from tiling_roofline_analysis_amd import inputs, roofline
