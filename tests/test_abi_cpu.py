@@ -55,9 +55,11 @@ def test_describe_plans():
     d = tra.tra_gemm_describe(tra.MFMA, 4096, 4096, 4096)
     assert "gemm_mfma_f32" in d and "tile=128x128x16" in d and "grid=1024" in d
     d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 1024)
-    assert "tile=64x64x64" in d and "grid=256" in d and "block=512" in d
+    assert "tile=64x64x32" in d and "2 K groups" in d and "grid=256" in d and "block=512" in d
+    d = tra.tra_gemm_describe(tra.MFMA, 2048, 2048, 2048)
+    assert "tile=128x128x16" in d and "8 waves" in d and "grid=256" in d and "block=512" in d
     d = tra.tra_gemm_describe(tra.MFMA, 16384, 64, 16384)
-    assert "tile=64x64x64" in d and "grid=256" in d
+    assert "tile=64x64x32" in d and "2 K groups" in d and "grid=256" in d
     d = tra.tra_gemm_describe(tra.MFMA, 3000, 2049, 1531)
     assert "tile=64x64x32" in d and "grid=1551" in d and "block=256" in d
     d = tra.tra_gemm_describe(tra.NAIVE, 1024, 1024, 1024)
@@ -77,10 +79,10 @@ def test_describe_plans():
     # whole waves of tiles: no split, no workspace
     d = tra.tra_gemm_describe(tra.MFMA_STREAMK, 4096, 4096, 4096)
     assert "stream_k_tiles=0" in d and "workspace_bytes=0" in d
-    # fewer tiles than a wave: all of them split (40 tiles x 4 slices over
-    # 80 workgroups of at least 2 slices)
+    # fewer tiles than a wave: all of them split (40 tiles x 7 slices of 32
+    # over 140 workgroups of at least 2 slices)
     d = tra.tra_gemm_describe(tra.MFMA_STREAMK, 300, 500, 203)
-    assert "stream_k_tiles=40" in d and "stream_k_wgs=80" in d
+    assert "stream_k_tiles=40" in d and "stream_k_wgs=140" in d
     assert "stream_k_tiles=0" in tra.tra_gemm_describe(tra.MFMA, 3000, 2049, 1531)
     with pytest.raises(tra.TraError):
         tra.tra_gemm_describe(7, 1, 1, 1)

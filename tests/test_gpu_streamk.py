@@ -38,8 +38,8 @@ def check_tol(C, ref, what):
 # each gets on 256 CUs): fewer tiles than a wave (every tile split), a last
 # partial wave of a few tiles split many ways, and the large-tile class.
 SPLIT_SHAPES = [
-    (300, 500, 203),      # 40 tiles x 4 slices over 80 workgroups: 2 partial sums a tile
-    (257, 129, 1000),     # 15 tiles x 16 slices over 120 workgroups: 8 a tile
+    (300, 500, 203),      # 40 tiles x 7 slices over 140 workgroups: 3 or 4 partial sums a tile
+    (257, 129, 1000),     # 15 tiles x 32 slices over 120 workgroups: 8 a tile
     (1500, 1500, 77),     # 576 tiles of 64 x 64: the last 64 over 96 workgroups
     (3000, 2049, 1531),   # the ragged shape: its last 15 tiles over 120 workgroups
     (4000, 4200, 203),    # 1056 tiles of 128 x 128: the last 32 over 208 workgroups

@@ -73,11 +73,12 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int KG_, int NR_>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int KG_, int NR_, int IL_ = 0>
 struct MfmaTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
     static constexpr int KG = KG_;                         // K groups of waves
     static constexpr int NR = NR_;                         // register sets in flight
+    static constexpr int IL = IL_;                         // interleaved issue order
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
     static constexpr int WAVES = WAVES_M * WAVES_N;        // waves per K group
     static constexpr int THREADS = 64 * WAVES * KG;
@@ -235,6 +236,37 @@ __device__ __forceinline__ void mfmas(const Frag<T> &fr, f32x16 (&acc)[T::FM][T:
                                                                  acc[i][j], 0, 0, 0);
 }
 
+// Interleaved issue order of one full iteration (IL tiles): each MFMA of
+// the slice is followed by a share of the memory instructions -- the LDS
+// reads of the next slice's fragments after the first half of the MFMAs,
+// the LDS stores and global loads after the second half -- so that no
+// burst of memory instructions leaves the matrix pipe idle.
+template <int I, int NM, int RPM, int WPM, int VPM>
+__device__ __forceinline__ void il_schedule() {
+    if constexpr (I < NM) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+        if constexpr (I < NM / 2) {
+            __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);    // LDS reads
+        } else {
+            __builtin_amdgcn_sched_group_barrier(0x200, WPM, 0);    // LDS writes
+            __builtin_amdgcn_sched_group_barrier(0x020, VPM, 0);    // global loads
+        }
+        il_schedule<I + 1, NM, RPM, WPM, VPM>();
+    }
+}
+
+template <class T, int MODE>
+__device__ __forceinline__ void il_order() {
+    constexpr int NM = T::HALF * T::FM * T::FN;
+    constexpr int HALF_M = NM / 2 > 0 ? NM / 2 : 1;
+    constexpr int NDR = T::FM * (T::HALF / 4) + (T::HALF * T::FN + 1) / 2;
+    constexpr int NDW = T::A_F4 + T::B_F4;
+    constexpr int NVM = (MODE == kVec ? 1 : 4) * (T::A_F4 + T::B_F4);
+    constexpr int SECOND = NM - NM / 2 > 0 ? NM - NM / 2 : 1;
+    il_schedule<0, NM, (NDR + HALF_M - 1) / HALF_M, (NDW + SECOND - 1) / SECOND,
+                (NVM + SECOND - 1) / SECOND>();
+}
+
 // The K loop over slices s0 .. s0+n-1 of one block tile (n >= 1).  Full
 // slices load in MODE; the slice that runs past K (the last one when K is
 // not a multiple of BK) loads with every index checked.
@@ -278,6 +310,17 @@ __device__ __forceinline__ void k_loop(const Ctx<T> &c, float *lds, int arow, in
     // MFMAs below the workgroup barrier, which makes them wait for the
     // global loads and LDS stores instead of covering them.)
     auto step = [&](int64_t s, int fp, int rp, bool guarded) {
+        if (T::IL && !guarded) {
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags<T>(lds, fp ^ 1, arow, bcol, kbase, fr[fp ^ 1]);
+            mfmas<T, 0, T::HALF>(fr[fp], acc);
+            stage<T>(lds, fp, c.t, ra[rp], rb[rp]);
+            fetch<T, MODE>(c, (s0 + s + 2 + NR) * BK, ra[rp], rb[rp]);
+            il_order<T, MODE>();
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            return;
+        }
         if (!guarded || s + 1 < n) read_frags<T>(lds, fp ^ 1, arow, bcol, kbase, fr[fp ^ 1]);
         __builtin_amdgcn_sched_barrier(0);
         mfmas<T, 0, T::HALF / 2>(fr[fp], acc);
@@ -607,25 +650,31 @@ void gemm_mfma_f32_sk(int64_t M, int64_t N, int64_t K,
     }
 }
 
-// Tile shapes (chosen by timing candidates on MI355X):
-//   Large  128x128x16, 4 waves of 64x64, two register sets, 2 workgroups per
-//          CU: shapes with at least 4 such tiles per CU (4096^3).
+// Tile shapes (chosen by timing candidates on MI355X, interleaved and
+// repeated on one warm GPU); every class issues its main loop in the
+// interleaved order (il_order), which measured 1-16% faster than the
+// blocked order on every shape:
+//   Large  128x128x16, 4 waves of 64x64, two register sets, 2 workgroups
+//          per CU: shapes with at least 4 such tiles per CU (4096^3).
+//   Mid    128x128x16, 8 waves of 64x32: about one such tile per CU
+//          (2048^3: 256 tiles).
 //   Many   64x64x32, 4 waves of 32x32: many small tiles and short K
 //          (3000x2049x1531).
-//   Few    64x64x64, four K groups of 2 waves of 32x64 (8 waves), one
-//          register set: about one tile per CU or long K (1024^3,
-//          16384x64x16384).
-using TileLarge = MfmaTile<128, 128, 16, 64, 64, 1, 2>;
-using TileMany = MfmaTile<64, 64, 32, 32, 32, 1, 2>;
-using TileFew = MfmaTile<64, 64, 64, 32, 64, 4, 1>;
+//   Few    64x64x32, two K groups of 4 waves of 32x32, four register sets:
+//          about one small tile per CU, any K (1024^3, 16384x64x16384).
+using TileLarge = MfmaTile<128, 128, 16, 64, 64, 1, 2, 1>;
+using TileMid = MfmaTile<128, 128, 16, 64, 32, 1, 2, 1>;
+using TileMany = MfmaTile<64, 64, 32, 32, 32, 1, 2, 1>;
+using TileFew = MfmaTile<64, 64, 32, 32, 32, 2, 4, 1>;
 
 constexpr int64_t kMi355xCUs = 256;
 
-enum class Shape { kLarge, kMany, kFew };
+enum class Shape { kLarge, kMid, kMany, kFew };
 
 Shape pick(int64_t M, int64_t N, int64_t K) {
     const int64_t large_tiles = ceil_div(M, TileLarge::BM) * ceil_div(N, TileLarge::BN);
     if (large_tiles >= 4 * kMi355xCUs) return Shape::kLarge;
+    if (4 * large_tiles > 3 * kMi355xCUs && large_tiles <= kMi355xCUs) return Shape::kMid;
     const int64_t small_tiles = ceil_div(M, TileMany::BM) * ceil_div(N, TileMany::BN);
     if (small_tiles > 2 * kMi355xCUs && K < 4096) return Shape::kMany;
     return Shape::kFew;
@@ -664,9 +713,13 @@ int64_t resident_per_cu(int fallback) {
     return n;
 }
 
+// Without a device: the stream-K kernel is held at 2 waves per SIMD, so
+// 2 workgroups of 4 waves or 1 of 8 fit a CU when LDS allows.
 template <class T>
 int resident_fallback() {
-    return T::KG > 1 ? 1 : 2;   // measured on gfx950 for the three tile classes
+    const int by_waves = 8 / (T::THREADS / 64);
+    const int by_lds = static_cast<int>(160 * 1024 / (T::LDS_WORDS * sizeof(float)));
+    return std::max(1, std::min(by_waves, by_lds));
 }
 
 // The work split of a launch.  Without stream-K, or when the tiles fill
@@ -752,10 +805,12 @@ LaunchPlan plan_mfma(int64_t M, int64_t N, int64_t K, bool stream_k) {
     switch (pick(M, N, K)) {
         case Shape::kLarge:
             return plan_for<TileLarge>(M, N, K, stream_k, "gemm_mfma_f32<128x128x16, 4 waves>");
+        case Shape::kMid:
+            return plan_for<TileMid>(M, N, K, stream_k, "gemm_mfma_f32<128x128x16, 8 waves>");
         case Shape::kMany:
             return plan_for<TileMany>(M, N, K, stream_k, "gemm_mfma_f32<64x64x32, 4 waves>");
         default:
-            return plan_for<TileFew>(M, N, K, stream_k, "gemm_mfma_f32<64x64x64, 4 K groups>");
+            return plan_for<TileFew>(M, N, K, stream_k, "gemm_mfma_f32<64x64x32, 2 K groups>");
     }
 }
 
@@ -781,6 +836,7 @@ bool stream_k_pays(int64_t M, int64_t N, int64_t K) {
 bool prefer_stream_k(int64_t M, int64_t N, int64_t K) {
     switch (pick(M, N, K)) {
         case Shape::kLarge: return stream_k_pays<TileLarge>(M, N, K);
+        case Shape::kMid: return stream_k_pays<TileMid>(M, N, K);
         case Shape::kMany: return stream_k_pays<TileMany>(M, N, K);
         default: return stream_k_pays<TileFew>(M, N, K);
     }
@@ -789,6 +845,7 @@ bool prefer_stream_k(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_mfma(const GemmArgs &a, bool stream_k, void *ws, size_t ws_bytes) {
     switch (pick(a.M, a.N, a.K)) {
         case Shape::kLarge: return launch_tile<TileLarge>(a, stream_k, ws, ws_bytes);
+        case Shape::kMid: return launch_tile<TileMid>(a, stream_k, ws, ws_bytes);
         case Shape::kMany: return launch_tile<TileMany>(a, stream_k, ws, ws_bytes);
         default: return launch_tile<TileFew>(a, stream_k, ws, ws_bytes);
     }
