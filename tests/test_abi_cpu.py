@@ -53,13 +53,14 @@ def test_status_and_variant_names():
 
 def test_describe_plans():
     d = tra.tra_gemm_describe(tra.MFMA, 4096, 4096, 4096)
-    assert "gemm_mfma_f32" in d and "tile=128x128x16" in d and "grid=1024" in d
+    assert "gemm_mfma_f32" in d and "tile=256x128x16" in d and "grid=512" in d
+    assert "block=512" in d
     d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 1024)
-    assert "tile=64x64x32" in d and "2 K groups" in d and "grid=256" in d and "block=512" in d
+    assert "tile=64x64x32" in d and "grid=256" in d and "block=256" in d
     d = tra.tra_gemm_describe(tra.MFMA, 2048, 2048, 2048)
     assert "tile=128x128x16" in d and "8 waves" in d and "grid=256" in d and "block=512" in d
     d = tra.tra_gemm_describe(tra.MFMA, 16384, 64, 16384)
-    assert "tile=64x64x32" in d and "2 K groups" in d and "grid=256" in d
+    assert "tile=64x64x32" in d and "grid=256" in d
     d = tra.tra_gemm_describe(tra.MFMA, 3000, 2049, 1531)
     assert "tile=64x64x32" in d and "grid=1551" in d and "block=256" in d
     d = tra.tra_gemm_describe(tra.NAIVE, 1024, 1024, 1024)

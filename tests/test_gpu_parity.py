@@ -222,11 +222,11 @@ def test_edge_sizes(variant):
 # Shapes that send the MFMA rung to each of its tile shapes, with tails on
 # every axis: (M, N, K, expected tile).
 MFMA_TILE_SHAPES = [
-    (4000, 4200, 203, "<128x128x16, 4 waves>"),   # 32 x 33 = 1056 tiles of 128 x 128
+    (4000, 4200, 203, "<256x128x16, 8 waves>"),   # 16 x 33 = 528 tiles of 256 x 128
     (1900, 2000, 300, "<128x128x16, 8 waves>"),   # 15 x 16 = 240 tiles of 128 x 128
     (1500, 1500, 77, "<64x64x32, 4 waves>"),      # 576 tiles of 64 x 64, short K
-    (200, 300, 4100, "<64x64x32, 2 K groups>"),   # few tiles, long K
-    (300, 500, 203, "<64x64x32, 2 K groups>"),    # few tiles, short K
+    (200, 300, 4100, "<64x64x32, 4 waves>"),      # few tiles, long K
+    (300, 500, 203, "<64x64x32, 4 waves>"),       # few tiles
 ]
 
 

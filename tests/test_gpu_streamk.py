@@ -42,7 +42,7 @@ SPLIT_SHAPES = [
     (257, 129, 1000),     # 15 tiles x 32 slices over 120 workgroups: 8 a tile
     (1500, 1500, 77),     # 576 tiles of 64 x 64: the last 64 over 96 workgroups
     (3000, 2049, 1531),   # the ragged shape: its last 15 tiles over 120 workgroups
-    (4000, 4200, 203),    # 1056 tiles of 128 x 128: the last 32 over 208 workgroups
+    (4000, 4200, 203),    # 528 tiles of 256 x 128: the last 16 over 104 workgroups
 ]
 
 

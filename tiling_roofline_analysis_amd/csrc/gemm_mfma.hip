@@ -237,21 +237,26 @@ __device__ __forceinline__ void mfmas(const Frag<T> &fr, f32x16 (&acc)[T::FM][T:
 }
 
 // Interleaved issue order of one full iteration (IL tiles): each MFMA of
-// the slice is followed by a share of the memory instructions -- the LDS
-// reads of the next slice's fragments after the first half of the MFMAs,
-// the LDS stores and global loads after the second half -- so that no
+// the slice is followed by a share of the memory instructions, so that no
 // burst of memory instructions leaves the matrix pipe idle.
-template <int I, int NM, int RPM, int WPM, int VPM>
+//   IL 1: the LDS reads of the next slice's fragments after the first half
+//         of the MFMAs, the LDS stores and global loads after the second;
+//   IL 2: the LDS reads spread over all MFMAs, the stores and global loads
+//         over the second half;
+//   IL 3: the LDS stores and global loads after the first half, the LDS
+//         reads after the second.
+template <int I, int NM, int IL, int RPM, int WPM, int VPM>
 __device__ __forceinline__ void il_schedule() {
     if constexpr (I < NM) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
-        if constexpr (I < NM / 2) {
-            __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);    // LDS reads
-        } else {
-            __builtin_amdgcn_sched_group_barrier(0x200, WPM, 0);    // LDS writes
-            __builtin_amdgcn_sched_group_barrier(0x020, VPM, 0);    // global loads
+        constexpr bool first = I < NM / 2;
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // one MFMA
+        if constexpr (IL == 2 || (IL == 1 && first) || (IL == 3 && !first))
+            __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);        // LDS reads
+        if constexpr ((IL != 3 && !first) || (IL == 3 && first)) {
+            __builtin_amdgcn_sched_group_barrier(0x200, WPM, 0);        // LDS stores
+            __builtin_amdgcn_sched_group_barrier(0x020, VPM, 0);        // global loads
         }
-        il_schedule<I + 1, NM, RPM, WPM, VPM>();
+        il_schedule<I + 1, NM, IL, RPM, WPM, VPM>();
     }
 }
 
@@ -259,12 +264,13 @@ template <class T, int MODE>
 __device__ __forceinline__ void il_order() {
     constexpr int NM = T::HALF * T::FM * T::FN;
     constexpr int HALF_M = NM / 2 > 0 ? NM / 2 : 1;
+    constexpr int READ_OVER = T::IL == 2 ? NM : HALF_M;
     constexpr int NDR = T::FM * (T::HALF / 4) + (T::HALF * T::FN + 1) / 2;
     constexpr int NDW = T::A_F4 + T::B_F4;
     constexpr int NVM = (MODE == kVec ? 1 : 4) * (T::A_F4 + T::B_F4);
-    constexpr int SECOND = NM - NM / 2 > 0 ? NM - NM / 2 : 1;
-    il_schedule<0, NM, (NDR + HALF_M - 1) / HALF_M, (NDW + SECOND - 1) / SECOND,
-                (NVM + SECOND - 1) / SECOND>();
+    constexpr int STORE_OVER = NM - NM / 2 > 0 ? NM - NM / 2 : 1;
+    il_schedule<0, NM, T::IL, (NDR + READ_OVER - 1) / READ_OVER,
+                (NDW + STORE_OVER - 1) / STORE_OVER, (NVM + STORE_OVER - 1) / STORE_OVER>();
 }
 
 // The K loop over slices s0 .. s0+n-1 of one block tile (n >= 1).  Full
@@ -654,30 +660,25 @@ void gemm_mfma_f32_sk(int64_t M, int64_t N, int64_t K,
 // repeated on one warm GPU); every class issues its main loop in the
 // interleaved order (il_order), which measured 1-16% faster than the
 // blocked order on every shape:
-//   Large  128x128x16, 4 waves of 64x64, two register sets, 2 workgroups
-//          per CU: shapes with at least 4 such tiles per CU (4096^3).
-//   Mid    128x128x16, 8 waves of 64x32: about one such tile per CU
+//   Large  256x128x16, 8 waves of 64x64, two register sets: shapes with at
+//          least 4 tiles of 128x128 per CU (4096^3: 512 such tiles).
+//   Mid    128x128x16, 8 waves of 64x32: about one 128x128 tile per CU
 //          (2048^3: 256 tiles).
-//   Many   64x64x32, 4 waves of 32x32: many small tiles and short K
-//          (3000x2049x1531).
-//   Few    64x64x32, two K groups of 4 waves of 32x32, four register sets:
-//          about one small tile per CU, any K (1024^3, 16384x64x16384).
-using TileLarge = MfmaTile<128, 128, 16, 64, 64, 1, 2, 1>;
+//   Many   64x64x32, 4 waves of 32x32, two register sets: every other
+//          shape (1024^3, 3000x2049x1531, 16384x64x16384).
+using TileLarge = MfmaTile<256, 128, 16, 64, 64, 1, 2, 1>;
 using TileMid = MfmaTile<128, 128, 16, 64, 32, 1, 2, 1>;
 using TileMany = MfmaTile<64, 64, 32, 32, 32, 1, 2, 1>;
-using TileFew = MfmaTile<64, 64, 32, 32, 32, 2, 4, 1>;
 
 constexpr int64_t kMi355xCUs = 256;
 
-enum class Shape { kLarge, kMid, kMany, kFew };
+enum class Shape { kLarge, kMid, kMany };
 
-Shape pick(int64_t M, int64_t N, int64_t K) {
-    const int64_t large_tiles = ceil_div(M, TileLarge::BM) * ceil_div(N, TileLarge::BN);
-    if (large_tiles >= 4 * kMi355xCUs) return Shape::kLarge;
-    if (4 * large_tiles > 3 * kMi355xCUs && large_tiles <= kMi355xCUs) return Shape::kMid;
-    const int64_t small_tiles = ceil_div(M, TileMany::BM) * ceil_div(N, TileMany::BN);
-    if (small_tiles > 2 * kMi355xCUs && K < 4096) return Shape::kMany;
-    return Shape::kFew;
+Shape pick(int64_t M, int64_t N, int64_t /*K*/) {
+    const int64_t tiles128 = ceil_div(M, 128) * ceil_div(N, 128);
+    if (tiles128 >= 4 * kMi355xCUs) return Shape::kLarge;
+    if (4 * tiles128 > 3 * kMi355xCUs && tiles128 <= kMi355xCUs) return Shape::kMid;
+    return Shape::kMany;
 }
 
 // Compute units of the current device (MI355X's 256 if it cannot be read).
@@ -804,13 +805,11 @@ hipError_t launch_tile(const GemmArgs &a, bool stream_k, void *ws, size_t ws_byt
 LaunchPlan plan_mfma(int64_t M, int64_t N, int64_t K, bool stream_k) {
     switch (pick(M, N, K)) {
         case Shape::kLarge:
-            return plan_for<TileLarge>(M, N, K, stream_k, "gemm_mfma_f32<128x128x16, 4 waves>");
+            return plan_for<TileLarge>(M, N, K, stream_k, "gemm_mfma_f32<256x128x16, 8 waves>");
         case Shape::kMid:
             return plan_for<TileMid>(M, N, K, stream_k, "gemm_mfma_f32<128x128x16, 8 waves>");
-        case Shape::kMany:
-            return plan_for<TileMany>(M, N, K, stream_k, "gemm_mfma_f32<64x64x32, 4 waves>");
         default:
-            return plan_for<TileFew>(M, N, K, stream_k, "gemm_mfma_f32<64x64x32, 2 K groups>");
+            return plan_for<TileMany>(M, N, K, stream_k, "gemm_mfma_f32<64x64x32, 4 waves>");
     }
 }
 
@@ -837,8 +836,7 @@ bool prefer_stream_k(int64_t M, int64_t N, int64_t K) {
     switch (pick(M, N, K)) {
         case Shape::kLarge: return stream_k_pays<TileLarge>(M, N, K);
         case Shape::kMid: return stream_k_pays<TileMid>(M, N, K);
-        case Shape::kMany: return stream_k_pays<TileMany>(M, N, K);
-        default: return stream_k_pays<TileFew>(M, N, K);
+        default: return stream_k_pays<TileMany>(M, N, K);
     }
 }
 
@@ -846,8 +844,7 @@ hipError_t launch_mfma(const GemmArgs &a, bool stream_k, void *ws, size_t ws_byt
     switch (pick(a.M, a.N, a.K)) {
         case Shape::kLarge: return launch_tile<TileLarge>(a, stream_k, ws, ws_bytes);
         case Shape::kMid: return launch_tile<TileMid>(a, stream_k, ws, ws_bytes);
-        case Shape::kMany: return launch_tile<TileMany>(a, stream_k, ws, ws_bytes);
-        default: return launch_tile<TileFew>(a, stream_k, ws, ws_bytes);
+        default: return launch_tile<TileMany>(a, stream_k, ws, ws_bytes);
     }
 }
 
