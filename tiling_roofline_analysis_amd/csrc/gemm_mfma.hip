@@ -17,17 +17,12 @@
 //   B operand:  lane l supplies B[h][l % 32]
 //   result:     lane l, word r holds C[8*(r/4) + 4*h + r%4][l % 32]
 // A wave owns a WM x WN piece of the block tile as (WM/32) x (WN/32) such
-// accumulators; the block has (BM/WM) x (BN/WN) waves per K group.
+// accumulators; the block has (BM/WM) x (BN/WN) waves.
 //
-// K groups (KG): the waves of a block form KG groups; group g takes the k
-// range [g*BK/KG, (g+1)*BK/KG) of every slice, and at the end groups
-// 1..KG-1 hand their partial sums to group 0 through LDS, added in group
-// order (deterministic).  More waves per CU without smaller tiles.
-//
-// K order inside a group's part of a slice (SUB = BK/KG wide): MFMA step q
-// (0 <= q < SUB/2) gives lane half h the k index g*SUB + h*SUB/2 + q.  Any
-// bijection of k is the same sum; this one lets a lane fetch its A values for
-// the slice as contiguous words (ds_read_b128) instead of one per step.
+// K order inside a slice: MFMA step q (0 <= q < BK/2) gives lane half h the
+// k index h*BK/2 + q.  Any bijection of k is the same sum; this one lets a
+// lane fetch its A values for the slice as contiguous words (ds_read_b128)
+// instead of one per step.
 //
 // LDS layout (two buffers):
 //   As[m][k]  k contiguous, row stride BK + 4 words: a global float4 along k
@@ -73,24 +68,20 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int KG_, int NR_, int IL_ = 0>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int NR_>
 struct MfmaTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
-    static constexpr int KG = KG_;                         // K groups of waves
     static constexpr int NR = NR_;                         // register sets in flight
-    static constexpr int IL = IL_;                         // interleaved issue order
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
-    static constexpr int WAVES = WAVES_M * WAVES_N;        // waves per K group
-    static constexpr int THREADS = 64 * WAVES * KG;
+    static constexpr int WAVES = WAVES_M * WAVES_N;
+    static constexpr int THREADS = 64 * WAVES;
     static constexpr int FM = WM / 32, FN = WN / 32;       // accumulators per wave
-    static constexpr int SUB = BK / KG, HALF = SUB / 2;    // k per group per slice
+    static constexpr int HALF = BK / 2;                    // MFMA steps per slice
     static constexpr int AST = BK + 4, BST = BN + 4;       // LDS row strides (words)
     static constexpr int A_VEC = BM * BK / 4, B_VEC = BK * BN / 4;   // float4 per slice
     static constexpr int A_F4 = (A_VEC + THREADS - 1) / THREADS;     // per lane
     static constexpr int B_F4 = (B_VEC + THREADS - 1) / THREADS;
-    static constexpr int STAGE_WORDS = 2 * (BM * AST + BK * BST);
-    static constexpr int RED_WORDS = (KG - 1) * BM * BN;            // K-group hand-off
-    static constexpr int LDS_WORDS = STAGE_WORDS > RED_WORDS ? STAGE_WORDS : RED_WORDS;
+    static constexpr int LDS_WORDS = 2 * (BM * AST + BK * BST);
     static constexpr int UNROLL = NR == 4 ? 4 : 2;
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be 32x32 blocks");
     static_assert(BM % WM == 0 && BN % WN == 0, "block tile must be whole wave tiles");
@@ -236,41 +227,36 @@ __device__ __forceinline__ void mfmas(const Frag<T> &fr, f32x16 (&acc)[T::FM][T:
                                                                  acc[i][j], 0, 0, 0);
 }
 
-// Interleaved issue order of one full iteration (IL tiles): each MFMA of
-// the slice is followed by a share of the memory instructions, so that no
-// burst of memory instructions leaves the matrix pipe idle.
-//   IL 1: the LDS reads of the next slice's fragments after the first half
-//         of the MFMAs, the LDS stores and global loads after the second;
-//   IL 2: the LDS reads spread over all MFMAs, the stores and global loads
-//         over the second half;
-//   IL 3: the LDS stores and global loads after the first half, the LDS
-//         reads after the second.
-template <int I, int NM, int IL, int RPM, int WPM, int VPM>
+// Issue order of one full iteration: each MFMA of the slice is followed by
+// a share of the memory instructions -- the LDS reads of the next slice's
+// fragments after the first half of the MFMAs, the LDS stores and global
+// loads after the second half -- so that no burst of memory instructions
+// leaves the matrix pipe idle.  (Measured against issuing them in blocks
+// between the halves: 1-16% faster on every tile shape.)
+template <int I, int NM, int RPM, int WPM, int VPM>
 __device__ __forceinline__ void il_schedule() {
     if constexpr (I < NM) {
-        constexpr bool first = I < NM / 2;
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // one MFMA
-        if constexpr (IL == 2 || (IL == 1 && first) || (IL == 3 && !first))
-            __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);        // LDS reads
-        if constexpr ((IL != 3 && !first) || (IL == 3 && first)) {
-            __builtin_amdgcn_sched_group_barrier(0x200, WPM, 0);        // LDS stores
-            __builtin_amdgcn_sched_group_barrier(0x020, VPM, 0);        // global loads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+        if constexpr (I < NM / 2) {
+            __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);    // LDS reads
+        } else {
+            __builtin_amdgcn_sched_group_barrier(0x200, WPM, 0);    // LDS stores
+            __builtin_amdgcn_sched_group_barrier(0x020, VPM, 0);    // global loads
         }
-        il_schedule<I + 1, NM, IL, RPM, WPM, VPM>();
+        il_schedule<I + 1, NM, RPM, WPM, VPM>();
     }
 }
 
 template <class T, int MODE>
 __device__ __forceinline__ void il_order() {
     constexpr int NM = T::HALF * T::FM * T::FN;
-    constexpr int HALF_M = NM / 2 > 0 ? NM / 2 : 1;
-    constexpr int READ_OVER = T::IL == 2 ? NM : HALF_M;
+    constexpr int FIRST = NM / 2 > 0 ? NM / 2 : 1;
+    constexpr int SECOND = NM - NM / 2 > 0 ? NM - NM / 2 : 1;
     constexpr int NDR = T::FM * (T::HALF / 4) + (T::HALF * T::FN + 1) / 2;
     constexpr int NDW = T::A_F4 + T::B_F4;
     constexpr int NVM = (MODE == kVec ? 1 : 4) * (T::A_F4 + T::B_F4);
-    constexpr int STORE_OVER = NM - NM / 2 > 0 ? NM - NM / 2 : 1;
-    il_schedule<0, NM, T::IL, (NDR + READ_OVER - 1) / READ_OVER,
-                (NDW + STORE_OVER - 1) / STORE_OVER, (NVM + STORE_OVER - 1) / STORE_OVER>();
+    il_schedule<0, NM, (NDR + FIRST - 1) / FIRST, (NDW + SECOND - 1) / SECOND,
+                (NVM + SECOND - 1) / SECOND>();
 }
 
 // The K loop over slices s0 .. s0+n-1 of one block tile (n >= 1).  Full
@@ -309,14 +295,17 @@ __device__ __forceinline__ void k_loop(const Ctx<T> &c, float *lds, int arow, in
     __syncthreads();   // buffer 0 is rewritten in iteration 0
 
     // Iteration s: fragment set s % 2, register set of slice s+2 is
-    // (s+2) % NR.  `guarded` only in the last few iterations.  The order is
-    // pinned with scheduling barriers: the fragment reads, the first half of
-    // the MFMAs, the LDS stores and global loads, the second half of the
-    // MFMAs, the workgroup barrier.  (Left alone, the compiler sinks the
-    // MFMAs below the workgroup barrier, which makes them wait for the
-    // global loads and LDS stores instead of covering them.)
+    // (s+2) % NR.  Each iteration reads the fragments of slice s+1, runs
+    // the MFMAs of slice s, stores slice s+2 to LDS, fetches slice s+2+NR
+    // and ends at a workgroup barrier.  Full iterations are issued in the
+    // interleaved order of il_order; the last few (`guarded`, with checks)
+    // in blocks pinned by scheduling barriers: the fragment reads, half the
+    // MFMAs, the LDS stores and global loads, the other half.  (Left alone,
+    // the compiler sinks the MFMAs below the workgroup barrier, which makes
+    // them wait for the global loads and LDS stores instead of covering
+    // them.)
     auto step = [&](int64_t s, int fp, int rp, bool guarded) {
-        if (T::IL && !guarded) {
+        if (!guarded) {
             __builtin_amdgcn_sched_barrier(0);
             read_frags<T>(lds, fp ^ 1, arow, bcol, kbase, fr[fp ^ 1]);
             mfmas<T, 0, T::HALF>(fr[fp], acc);
@@ -327,14 +316,13 @@ __device__ __forceinline__ void k_loop(const Ctx<T> &c, float *lds, int arow, in
             __syncthreads();
             return;
         }
-        if (!guarded || s + 1 < n) read_frags<T>(lds, fp ^ 1, arow, bcol, kbase, fr[fp ^ 1]);
+        if (s + 1 < n) read_frags<T>(lds, fp ^ 1, arow, bcol, kbase, fr[fp ^ 1]);
         __builtin_amdgcn_sched_barrier(0);
         mfmas<T, 0, T::HALF / 2>(fr[fp], acc);
         __builtin_amdgcn_sched_barrier(0);
-        if (!guarded || s + 2 < n) {
+        if (s + 2 < n) {
             stage<T>(lds, fp, c.t, ra[rp], rb[rp]);
-            if (!guarded) fetch<T, MODE>(c, (s0 + s + 2 + NR) * BK, ra[rp], rb[rp]);
-            else if (s + 2 + NR < n) fetch_any(s + 2 + NR, rp);
+            if (s + 2 + NR < n) fetch_any(s + 2 + NR, rp);
         }
         __builtin_amdgcn_sched_barrier(0);
         mfmas<T, T::HALF / 2, T::HALF>(fr[fp], acc);
@@ -426,16 +414,14 @@ __device__ __forceinline__ void tile_pass(const Ctx<T> &c, int vec_a, int vec_b,
                                           int64_t s0, int64_t n, float *out, int64_t ldo,
                                           int row_lo, int64_t rows, int col_lo, int64_t cols) {
     constexpr int BM = T::BM, BN = T::BN, WM = T::WM, WN = T::WN;
-    constexpr int FM = T::FM, FN = T::FN, KG = T::KG;
+    constexpr int FM = T::FM, FN = T::FN;
 
     const int t = c.t;
     const int lane = t & 63, wave = t >> 6;
     const int l32 = lane & 31, h = lane >> 5;
-    const int grp = wave / T::WAVES;            // K group of this wave
-    const int wig = wave % T::WAVES;            // wave within its group
-    const int wm0 = (wig / T::WAVES_N) * WM;
-    const int wn0 = (wig % T::WAVES_N) * WN;
-    const int kbase = grp * T::SUB + h * T::HALF;   // this lane's first k in a slice
+    const int wm0 = (wave / T::WAVES_N) * WM;
+    const int wn0 = (wave % T::WAVES_N) * WN;
+    const int kbase = h * T::HALF;              // this lane's first k in a slice
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -455,37 +441,6 @@ __device__ __forceinline__ void tile_pass(const Ctx<T> &c, int vec_a, int vec_b,
             k_loop<T, kVecA>(c, lds, wm0 + l32, wn0 + l32, kbase, acc, s0, n);
         else
             k_loop<T, kScalar>(c, lds, wm0 + l32, wn0 + l32, kbase, acc, s0, n);
-    }
-
-    if (KG > 1) {
-        // K groups 1..KG-1 hand their partial sums to group 0 through LDS
-        // (the K loop ended with a barrier after its last LDS read); group 0
-        // adds them in group order, one 32x32 block at a time.
-        constexpr int PER_WAVE = FM * FN * 16 * 64;
-        if (grp > 0) {
-            float *dst = lds + ((grp - 1) * T::WAVES + wig) * PER_WAVE + lane;
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) dst[((i * FN + j) * 16 + r) * 64] = acc[i][j][r];
-        }
-        __syncthreads();
-        if (grp > 0) return;
-        // A rolled loop over the groups keeps one group's values live at a
-        // time (unrolled, the compiler hoists every read and spills).
-#pragma unroll 1
-        for (int g = 1; g < KG; ++g) {
-            const float *src = lds + ((g - 1) * T::WAVES + wig) * PER_WAVE + lane;
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        acc[i][j][r] += src[((i * FN + j) * 16 + r) * 64];
-        }
     }
 
     // Epilogue: word r of accumulator (i, j) is row 8*(r/4) + 4*h + r%4,
@@ -657,18 +612,16 @@ void gemm_mfma_f32_sk(int64_t M, int64_t N, int64_t K,
 }
 
 // Tile shapes (chosen by timing candidates on MI355X, interleaved and
-// repeated on one warm GPU); every class issues its main loop in the
-// interleaved order (il_order), which measured 1-16% faster than the
-// blocked order on every shape:
+// repeated on one warm GPU):
 //   Large  256x128x16, 8 waves of 64x64, two register sets: shapes with at
 //          least 4 tiles of 128x128 per CU (4096^3: 512 such tiles).
 //   Mid    128x128x16, 8 waves of 64x32: about one 128x128 tile per CU
 //          (2048^3: 256 tiles).
 //   Many   64x64x32, 4 waves of 32x32, two register sets: every other
 //          shape (1024^3, 3000x2049x1531, 16384x64x16384).
-using TileLarge = MfmaTile<256, 128, 16, 64, 64, 1, 2, 1>;
-using TileMid = MfmaTile<128, 128, 16, 64, 32, 1, 2, 1>;
-using TileMany = MfmaTile<64, 64, 32, 32, 32, 1, 2, 1>;
+using TileLarge = MfmaTile<256, 128, 16, 64, 64, 2>;
+using TileMid = MfmaTile<128, 128, 16, 64, 32, 2>;
+using TileMany = MfmaTile<64, 64, 32, 32, 32, 2>;
 
 constexpr int64_t kMi355xCUs = 256;
 
