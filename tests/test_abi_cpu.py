@@ -60,7 +60,7 @@ def test_describe_plans():
     d = tra.tra_gemm_describe(tra.MFMA, 2048, 2048, 2048)
     assert "tile=128x128x16" in d and "8 waves" in d and "grid=256" in d and "block=512" in d
     d = tra.tra_gemm_describe(tra.MFMA, 16384, 64, 16384)
-    assert "tile=64x64x32" in d and "grid=256" in d
+    assert "tile=64x64x32" in d and "4 sets" in d and "grid=256" in d
     d = tra.tra_gemm_describe(tra.MFMA, 3000, 2049, 1531)
     assert "tile=64x64x32" in d and "grid=1551" in d and "block=256" in d
     d = tra.tra_gemm_describe(tra.NAIVE, 1024, 1024, 1024)
@@ -212,6 +212,10 @@ def test_caller_workspace_checked_on_host():
     ((1500, 1500, 77), "mfma"),            # 3 slices of K: nothing to share
     ((1152, 1152, 8192), "mfma_streamk"),  # 324 tiles of one workgroup a CU
     ((16384, 64, 16384), "mfma"),          # 256 tiles
+    ((200, 300, 4100), "mfma_streamk"),    # 20 tiles, 129 slices each
+    ((300, 500, 203), "mfma"),             # 40 tiles of 7 slices: too short to share
+    ((100, 100, 300), "mfma"),             # 4 tiles of 10 slices: saves < 8 us
+    ((100, 100, 2000), "mfma_streamk"),    # 4 tiles of 63 slices
 ])
 def test_auto_choice(shape, rung):
     d = tra.tra_gemm_describe(tra.AUTO, *shape)

@@ -618,20 +618,24 @@ void gemm_mfma_f32_sk(int64_t M, int64_t N, int64_t K,
 //   Mid    128x128x16, 8 waves of 64x32: about one 128x128 tile per CU
 //          (2048^3: 256 tiles).
 //   Many   64x64x32, 4 waves of 32x32, two register sets: every other
-//          shape (1024^3, 3000x2049x1531, 16384x64x16384).
+//          shape with K < 4096 (1024^3, 3000x2049x1531).
+//   Deep   the Many tile with four register sets in flight, for K >= 4096
+//          (16384x64x16384: the operands stream from HBM and need the
+//          longer prefetch).
 using TileLarge = MfmaTile<256, 128, 16, 64, 64, 2>;
 using TileMid = MfmaTile<128, 128, 16, 64, 32, 2>;
 using TileMany = MfmaTile<64, 64, 32, 32, 32, 2>;
+using TileDeep = MfmaTile<64, 64, 32, 32, 32, 4>;
 
 constexpr int64_t kMi355xCUs = 256;
 
-enum class Shape { kLarge, kMid, kMany };
+enum class Shape { kLarge, kMid, kMany, kDeep };
 
-Shape pick(int64_t M, int64_t N, int64_t /*K*/) {
+Shape pick(int64_t M, int64_t N, int64_t K) {
     const int64_t tiles128 = ceil_div(M, 128) * ceil_div(N, 128);
     if (tiles128 >= 4 * kMi355xCUs) return Shape::kLarge;
     if (4 * tiles128 > 3 * kMi355xCUs && tiles128 <= kMi355xCUs) return Shape::kMid;
-    return Shape::kMany;
+    return K >= 4096 ? Shape::kDeep : Shape::kMany;
 }
 
 // Compute units of the current device (MI355X's 256 if it cannot be read).
@@ -761,26 +765,39 @@ LaunchPlan plan_mfma(int64_t M, int64_t N, int64_t K, bool stream_k) {
             return plan_for<TileLarge>(M, N, K, stream_k, "gemm_mfma_f32<256x128x16, 8 waves>");
         case Shape::kMid:
             return plan_for<TileMid>(M, N, K, stream_k, "gemm_mfma_f32<128x128x16, 8 waves>");
-        default:
+        case Shape::kMany:
             return plan_for<TileMany>(M, N, K, stream_k, "gemm_mfma_f32<64x64x32, 4 waves>");
+        default:
+            return plan_for<TileDeep>(M, N, K, stream_k,
+                                      "gemm_mfma_f32<64x64x32, 4 waves, 4 sets>");
     }
 }
 
-// AUTO's choice, from timings of both forms on MI355X: the stream-K split
-// pays when one tile per workgroup would leave some CUs a whole tile more
-// work than the mean (at least 10% more: e.g. 1296 tiles on 256 CUs, 5.06 a
-// CU, so some CUs run 6), K has at least 8 slices to share out, and the
-// product is large enough (>= 4 GFLOP) to hide the second launch.  Shapes
-// that split evenly over the CUs, like 2304 tiles on 256, stay
-// data-parallel.
+// AUTO's choice, from timings of both forms on MI355X.  The split needs K
+// to have at least 8 slices to share out, and then pays
+//   * when fewer tiles than half the CUs would leave most CUs idle and the
+//     time that sharing saves -- (1 - tiles/CUs) of one tile's slices at
+//     the measured per-CU MFMA rate (148 TFLOP/s over 256 CUs) -- covers
+//     the second launch (8 us; 200x300x4100: 20 tiles, 67 -> ~20 us);
+//   * otherwise when one tile per workgroup would leave some CUs a whole
+//     tile more work than the mean (at least 10% more: e.g. 1296 tiles on
+//     256 CUs, 5.06 a CU, so some CUs run 6) and the product is large
+//     enough (>= 4 GFLOP) to hide the second launch.  Shapes that split
+//     evenly over the CUs, like 2304 tiles on 256, stay data-parallel.
 template <class T>
 bool stream_k_pays(int64_t M, int64_t N, int64_t K) {
     const SkPlan p = plan_split<T>(M, N, K, true);
     if (p.sk_tiles == 0 || p.ipt < 8) return false;
-    if (2.0 * static_cast<double>(M) * static_cast<double>(N) * static_cast<double>(K) < 4e9)
-        return false;
     const int64_t cus = device_cus();
     const int64_t tiles = static_cast<int64_t>(p.tiles_m) * p.tiles_n;
+    if (2 * tiles < cus) {
+        const double slice_s = 2.0 * T::BM * T::BN * T::BK / (148e12 / 256);
+        const double saved = (1.0 - static_cast<double>(tiles) / static_cast<double>(cus)) *
+                             static_cast<double>(p.ipt) * slice_s;
+        return saved >= 8e-6;
+    }
+    if (2.0 * static_cast<double>(M) * static_cast<double>(N) * static_cast<double>(K) < 4e9)
+        return false;
     const int64_t per_cu = ceil_div(tiles, cus);
     return static_cast<double>(per_cu * cus) >= 1.1 * static_cast<double>(tiles);
 }
@@ -789,7 +806,8 @@ bool prefer_stream_k(int64_t M, int64_t N, int64_t K) {
     switch (pick(M, N, K)) {
         case Shape::kLarge: return stream_k_pays<TileLarge>(M, N, K);
         case Shape::kMid: return stream_k_pays<TileMid>(M, N, K);
-        default: return stream_k_pays<TileMany>(M, N, K);
+        case Shape::kMany: return stream_k_pays<TileMany>(M, N, K);
+        default: return stream_k_pays<TileDeep>(M, N, K);
     }
 }
 
@@ -797,7 +815,8 @@ hipError_t launch_mfma(const GemmArgs &a, bool stream_k, void *ws, size_t ws_byt
     switch (pick(a.M, a.N, a.K)) {
         case Shape::kLarge: return launch_tile<TileLarge>(a, stream_k, ws, ws_bytes);
         case Shape::kMid: return launch_tile<TileMid>(a, stream_k, ws, ws_bytes);
-        default: return launch_tile<TileMany>(a, stream_k, ws, ws_bytes);
+        case Shape::kMany: return launch_tile<TileMany>(a, stream_k, ws, ws_bytes);
+        default: return launch_tile<TileDeep>(a, stream_k, ws, ws_bytes);
     }
 }
 
