@@ -11,7 +11,10 @@ M = N = K = 4096 with normal(0, 1) inputs is reported beside it as
 
 Timing: HIP events recorded on the stream the kernels are launched on
 (torch's current stream), around `--steps` back-to-back launches, after
-`--warmup` launches; per-launch event pairs give min/median.
+`--warmup` launches; per-launch event pairs give min/median.  Before the
+warm-up launches of each headline shape, the same GEMM runs untimed for
+`--warm-seconds` (0.5 s) so that timing starts at the GPU's sustained
+clocks rather than while they ramp up.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -36,7 +39,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def time_variant(tra, torch, variant, w, dA, dB, dC, steps, warmup):
+def time_variant(tra, torch, variant, w, dA, dB, dC, steps, warmup, warm_seconds=0.0):
     stream = torch.cuda.current_stream()
     handle = stream.cuda_stream
     pa, pb, pc = dA.data_ptr(), dB.data_ptr(), dC.data_ptr()
@@ -51,6 +54,13 @@ def time_variant(tra, torch, variant, w, dA, dB, dC, steps, warmup):
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize()
+    if warm_seconds > 0:
+        # bring the GPU to its sustained clocks with the same launch, untimed
+        t_end = time.perf_counter() + warm_seconds
+        while time.perf_counter() < t_end:
+            for _ in range(20):
+                launch()
+            torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -213,6 +223,9 @@ def main():
     ap.add_argument("--no-roofs", action="store_true", help="skip the roof probes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy 5 times (scales HBM counters)")
+    ap.add_argument("--warm-seconds", type=float, default=0.5,
+                    help="untimed launches of the headline GEMM before its warm-up steps, so "
+                         "the GPU runs at its sustained clocks when timing starts")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip host-inclusive timing and the torch / numpy comparisons")
     ap.add_argument("--plot", metavar="SVG", help="write the roofline chart of the ladder here")
@@ -246,7 +259,8 @@ def main():
         dB = torch.from_numpy(B).to("cuda:0")
         dC = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda:0")
         log(f"[{name}] {tra.tra_gemm_describe(tra.AUTO, w.M, w.N, w.K)}")
-        avg, mn, med = time_variant(tra, torch, tra.AUTO, w, dA, dB, dC, steps, warmup)
+        avg, mn, med = time_variant(tra, torch, tra.AUTO, w, dA, dB, dC, steps, warmup,
+                                    args.warm_seconds)
         rep = rl.gemm_roofline(w.M, w.N, w.K, avg * 1e-3)
         log(f"[{name}] auto(mfma): {avg * 1e3:.2f} us/launch (min {mn * 1e3:.2f}, "
             f"median {med * 1e3:.2f}) = {rep['tflops']:.2f} TFLOP/s, "
