@@ -37,7 +37,8 @@
 //                 fetch slice s+2+NR from global memory into the freed set;
 //                 run the MFMAs of slice s from registers;  barrier.
 // Each global load has NR iterations to arrive and every LDS access of an
-// iteration overlaps that iteration's MFMAs.
+// iteration overlaps that iteration's MFMAs; the memory instructions are
+// issued between the MFMAs (il_order) rather than in bursts.
 //
 // Global loads: a tile that would cross row M or column N is moved back
 // inside the matrices (its rows and columns shared with the neighbouring
