@@ -53,8 +53,9 @@ int resolve(int variant, int64_t M, int64_t N, int64_t K) {
     return tra::prefer_stream_k(M, N, K) ? TRA_GEMM_MFMA_STREAMK : TRA_GEMM_MFMA;
 }
 
-tra::LaunchPlan plan_of(int variant, int64_t M, int64_t N, int64_t K) {
-    switch (resolve(variant, M, N, K)) {
+// The launch plan of a resolved rung (not AUTO).
+tra::LaunchPlan plan_rung(int rung, int64_t M, int64_t N, int64_t K) {
+    switch (rung) {
         case TRA_GEMM_NAIVE: return tra::plan_naive(M, N, K);
         case TRA_GEMM_LDS_TILED: return tra::plan_lds_tiled(M, N, K);
         case TRA_GEMM_REGBLOCK_DB: return tra::plan_regblock(M, N, K);
@@ -123,10 +124,15 @@ tra_status hip_status(hipError_t err) {
     return TRA_ERR_HIP;
 }
 
-// Host-side checks; launches nothing.  On success M, N > 0.
+tra::LaunchPlan plan_of(int variant, int64_t M, int64_t N, int64_t K) {
+    return plan_rung(resolve(variant, M, N, K), M, N, K);
+}
+
+// Host-side checks; launches nothing.  On success with M, N > 0 (noop
+// false), `rung` is the rung to run and `plan` its launch.
 tra_status check_args(int variant, int64_t M, int64_t N, int64_t K, const float *A,
                       int64_t lda, const float *B, int64_t ldb, const float *C, int64_t ldc,
-                      bool &noop) {
+                      bool &noop, int &rung, tra::LaunchPlan &plan) {
     noop = false;
     if (!valid_variant(variant)) return TRA_ERR_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0) return TRA_ERR_INVALID_ARG;
@@ -144,8 +150,9 @@ tra_status check_args(int variant, int64_t M, int64_t N, int64_t K, const float 
             return TRA_ERR_INVALID_ARG;
         if (overlaps(ec, ea) || overlaps(ec, eb)) return TRA_ERR_INVALID_ARG;
     }
-    const tra::LaunchPlan p = plan_of(variant, M, N, K);
-    if (p.grid <= 0 || p.grid > tra::kMaxGrid) return TRA_ERR_UNSUPPORTED;
+    rung = resolve(variant, M, N, K);
+    plan = plan_rung(rung, M, N, K);
+    if (plan.grid <= 0 || plan.grid > tra::kMaxGrid) return TRA_ERR_UNSUPPORTED;
     return TRA_OK;
 }
 
@@ -159,12 +166,13 @@ tra_status gemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K, const 
                             int64_t lda, const float *B, int64_t ldb, float *C, int64_t ldc,
                             void *stream) {
     bool noop = false;
-    const tra_status st = check_args(variant, M, N, K, A, lda, B, ldb, C, ldc, noop);
+    int v = 0;
+    tra::LaunchPlan plan{};
+    const tra_status st = check_args(variant, M, N, K, A, lda, B, ldb, C, ldc, noop, v, plan);
     if (st != TRA_OK || noop) return st;
 
-    const int v = resolve(variant, M, N, K);
     const tra::GemmArgs a{M, N, K, A, lda, B, ldb, C, ldc, static_cast<hipStream_t>(stream)};
-    const size_t need = plan_of(v, M, N, K).workspace_bytes;
+    const size_t need = plan.workspace_bytes;
     if (need == 0) return hip_status(launch(v, a, nullptr, 0));
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     void *ws = nullptr;
@@ -177,11 +185,12 @@ tra_status gemm_f32_variant_ws(int variant, int64_t M, int64_t N, int64_t K, con
                                int64_t lda, const float *B, int64_t ldb, float *C, int64_t ldc,
                                void *workspace, size_t workspace_bytes, void *stream) {
     bool noop = false;
-    const tra_status st = check_args(variant, M, N, K, A, lda, B, ldb, C, ldc, noop);
+    int v = 0;
+    tra::LaunchPlan plan{};
+    const tra_status st = check_args(variant, M, N, K, A, lda, B, ldb, C, ldc, noop, v, plan);
     if (st != TRA_OK || noop) return st;
 
-    const int v = resolve(variant, M, N, K);
-    const size_t need = plan_of(v, M, N, K).workspace_bytes;
+    const size_t need = plan.workspace_bytes;
     if (need > 0 && (workspace == nullptr || workspace_bytes < need ||
                      (reinterpret_cast<uintptr_t>(workspace) & 15u) != 0))
         return TRA_ERR_INVALID_ARG;
@@ -207,12 +216,13 @@ tra_status tra_gemm_describe(int variant, int64_t M, int64_t N, int64_t K, char 
     if (!valid_variant(variant) || M < 0 || N < 0 || K < 0) return TRA_ERR_INVALID_ARG;
     if (buf == nullptr) return len == 0 ? TRA_OK : TRA_ERR_INVALID_ARG;
     if (len == 0) return TRA_OK;
-    const tra::LaunchPlan p = plan_of(variant, M, N, K);
+    const int rung = resolve(variant, M, N, K);
+    const tra::LaunchPlan p = plan_rung(rung, M, N, K);
     std::snprintf(buf, len,
                   "variant=%s rung=%s kernel=%s tile=%dx%dx%d grid=%lld block=%d lds_bytes=%d "
                   "split_k=%d stream_k_tiles=%lld stream_k_wgs=%lld workspace_bytes=%zu",
                   tra_gemm_variant_name(variant),
-                  tra_gemm_variant_name(resolve(variant, M, N, K)), p.kernel, p.bm, p.bn, p.bk,
+                  tra_gemm_variant_name(rung), p.kernel, p.bm, p.bn, p.bk,
                   static_cast<long long>(p.grid), p.block, p.lds_bytes, p.split_k,
                   static_cast<long long>(p.sk_tiles), static_cast<long long>(p.sk_wgs),
                   p.workspace_bytes);
