@@ -351,3 +351,40 @@ def test_invalid_call_leaves_c_untouched():
     assert torch.all(c == 3.0) and torch.all(a == 1.0)
     with pytest.raises(ValueError):
         tra.matmul(a[:, :7], b)       # inner dimensions differ
+
+
+# --- seeded random shapes: every MFMA path against the oracle -----------------
+
+def _random_shapes(seed, n):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        # sizes around the tile edges of every class, K across the slice edges
+        M = int(rng.choice([rng.integers(1, 70), rng.integers(60, 300), rng.integers(250, 700)]))
+        N = int(rng.choice([rng.integers(1, 70), rng.integers(60, 300), rng.integers(250, 700)]))
+        K = int(rng.choice([rng.integers(1, 40), rng.integers(30, 300), rng.integers(900, 1300)]))
+        aligned = bool(rng.integers(0, 2))
+        out.append((M, N, K, aligned))
+    return out
+
+
+@pytest.mark.parametrize("variant", [tra.AUTO, tra.MFMA, tra.MFMA_STREAMK],
+                         ids=["auto", "mfma", "mfma_streamk"])
+def test_random_shapes_small_ints_exact(variant):
+    """Seeded random shapes with tails on every axis, aligned and odd
+    strides; small-integer inputs make every partial sum exact, so the GPU
+    must equal the oracle bit for bit whatever the tile, split or order."""
+    for M, N, K, aligned in _random_shapes(2024, 24):
+        log(f"[case] {tra.tra_gemm_variant_name(variant)} {M}x{N}x{K} aligned={aligned} "
+            f"({tra.tra_gemm_describe(variant, M, N, K)})")
+        A = inputs.small_ints(M, K, M * 7919 + K)
+        B = inputs.small_ints(K, N, N * 7919 + K + 1)
+        ref = oracle.gemm(A, B)
+        if aligned:
+            lda, ldb, ldc, offs = (K + 3) // 4 * 4, (N + 3) // 4 * 4, (N + 3) // 4 * 4, (0, 0, 0)
+        else:
+            lda, ldb, ldc, offs = K + 1, N + 3, N + 2, (1, 2, 3)
+        C, buf, ldc_, off = run_gpu(variant, A, B, lda, ldb, ldc, offs)
+        assert_exact(C, ref.c32, f"{M}x{N}x{K} aligned={aligned}")
+        full = buf[off:off + M * ldc_].reshape(M, ldc_)
+        assert np.all(full[:, N:] == C_SENTINEL), "wrote past column N"
