@@ -355,7 +355,8 @@ __device__ __forceinline__ void k_loop(const Ctx<T> &c, float *lds, int arow, in
 // done one per workgroup ("data-parallel").  sk_tiles = 0 is the plain
 // one-tile-per-workgroup launch.
 // Counts that fit 32 bits: tiles (the grid is below 2^31) and stream-K
-// slices (the split is only planned when sk_tiles * ipt < 2^31).
+// slices (the split is only planned when sk_tiles * ipt < 2^30, which keeps
+// every intermediate of sk_begin / sk_owner below 2^31).
 struct SkPlan {
     int64_t ipt;        // K slices per tile, ceil(K / BK)
     float *ws;          // 2 * sk_wgs partial tiles, BM x BN row-major each
@@ -701,7 +702,7 @@ SkPlan plan_split(int64_t M, int64_t N, int64_t K, bool stream_k) {
     if (tiles % slots == 0) return p;
     const int64_t sk_tiles = tiles % slots;
     const int64_t total = sk_tiles * p.ipt;
-    if (total > kMaxGrid) return p;   // slice counts must fit 32 bits
+    if (total > (kMaxGrid >> 1)) return p;   // slice arithmetic must fit 32 bits
     const int64_t min_slices = std::max<int64_t>(2, ceil_div(p.ipt, 8));
     const int64_t sk_wgs = std::max<int64_t>(1, std::min(slots, total / min_slices));
     p.sk_tiles = static_cast<int>(sk_tiles);
