@@ -1,0 +1,103 @@
+"""Host-side tests of the rocprofv3 summaries (profiling.py) on small
+synthetic databases with the rocpd tables the summaries read."""
+import sqlite3
+
+import pytest
+
+import tiling_roofline_analysis_amd as tra
+from tiling_roofline_analysis_amd import inputs, profiling
+
+
+def _counters_db(path, rows):
+    c = sqlite3.connect(path)
+    c.execute("create table counters_collection (kernel_name text, grid_size int, "
+              "counter_name text, value real, duration real)")
+    c.executemany("insert into counters_collection values (?,?,?,?,?)", rows)
+    c.commit()
+    c.close()
+
+
+def _launches():
+    return list(profiling.ladder_launches())
+
+
+def _kernel_name(kernel):
+    return f"void tra::{kernel}<tra::Tile<1, 2> >(long, long, long, float const*)"
+
+
+def test_ladder_launches_cover_every_rung_at_both_shapes():
+    got = _launches()
+    assert len(got) == 2 * len(tra.LADDER)
+    for rung, wname, kernel, lanes in got:
+        w = inputs.WORKLOADS[wname]
+        assert kernel.startswith("gemm_")
+        assert lanes > 0 and lanes % 64 == 0
+        assert rung in [tra.tra_gemm_variant_name(v) for v in tra.LADDER]
+        assert w.M * w.N > 0
+
+
+def test_trace_summary(tmp_path):
+    db = tmp_path / "t.db"
+    c = sqlite3.connect(db)
+    c.execute("create table kernels (name text, grid_x int, grid_y int, grid_z int, "
+              "workgroup_x int, workgroup_y int, workgroup_z int, duration real)")
+    c.executemany("insert into kernels values (?,?,?,?,?,?,?,?)",
+                  [("k1(long)", 256, 1, 1, 256, 1, 1, d) for d in (1000.0, 3000.0)]
+                  + [("k2(long)", 64, 1, 1, 64, 1, 1, 500.0)])
+    c.commit()
+    c.close()
+    text = profiling.trace_summary(str(db), "cmd")
+    line = [x for x in text.splitlines() if "`k1`" in x][0]
+    cells = [x.strip() for x in line.strip("|").split("|")]
+    assert cells[1:] == ["256", "256", "2", "2.00", "1.00", "3.00"]
+    # ordered by total time: k1 (4 us) before k2 (0.5 us)
+    assert text.index("`k1`") < text.index("`k2`")
+
+
+def test_ladder_traffic_scales_by_the_copy(tmp_path):
+    copy = "__amd_rocclr_copyBuffer"
+    fetch, write = tmp_path / "f.db", tmp_path / "w.db"
+    # the copy's counters read half and all of what it moved
+    frows = [(copy, 1 << 20, "FETCH_SIZE", profiling.COPY_BYTES / 2048.0, 0.0)]
+    wrows = [(copy, 1 << 20, "WRITE_SIZE", profiling.COPY_BYTES / 1024.0, 0.0)]
+    for i, (rung, wname, kernel, lanes) in enumerate(_launches()):
+        frows.append((_kernel_name(kernel), lanes, "FETCH_SIZE", 100.0 + i, 0.0))
+        wrows.append((_kernel_name(kernel), lanes, "WRITE_SIZE", 10.0 + i, 0.0))
+    _counters_db(fetch, frows)
+    _counters_db(write, wrows)
+    data, fs, ws = profiling.ladder_traffic(str(fetch), str(write))
+    assert fs == pytest.approx(2.0) and ws == pytest.approx(1.0)
+    assert len(data) == len(_launches())
+    for i, (rung, wname, kernel, lanes) in enumerate(_launches()):
+        d = data[(rung, wname)]
+        assert d["read_bytes"] == pytest.approx((100.0 + i) * 1024 * 2)
+        assert d["write_bytes"] == pytest.approx((10.0 + i) * 1024)
+
+
+def test_counters_summary_ratios(tmp_path):
+    db = tmp_path / "c.db"
+    rows = []
+    clk = 1000.0
+    for rung, wname, kernel, lanes in _launches():
+        v = {"GRBM_GUI_ACTIVE": 8 * clk, "SQ_INSTS_LDS": 400.0, "SQ_LDS_BANK_CONFLICT": 100.0,
+             "SQ_WAIT_INST_LDS": 30.0, "SQ_WAVE_CYCLES": 300.0, "SQ_INSTS_VALU": 1024.0 * clk,
+             "SQ_INSTS_MFMA": 7.0, "SQ_VALU_MFMA_BUSY_CYCLES": 512.0 * clk,
+             "SQ_BUSY_CYCLES": 1.0}
+        rows += [(_kernel_name(kernel), lanes, n, x, 2400.0) for n, x in v.items()]
+    # a launch of another grid must not be mistaken for a rung
+    rows.append((_kernel_name("gemm_naive_f32"), 3, "SQ_INSTS_LDS", 1e9, 1.0))
+    _counters_db(db, rows)
+    got = profiling.ladder_counters(str(db))
+    assert len(got) == len(_launches())
+    text = profiling.counters_summary(str(db), "the command")
+    assert "the command" in text
+    body = [x for x in text.splitlines() if x.startswith("| ") and "---" not in x][1:]
+    assert len(body) == len(_launches())
+    for line in body:
+        cells = [x.strip() for x in line.strip("|").split("|")]
+        # duration 2.4 us; clk / 2.4 GHz = 1000 / 2400 us; 400 LDS instructions
+        assert cells[4:8] == ["2.4", "0.4", "400", "0.250"]
+        # LDS wait share, VALU per SIMD-clock (1024 SIMDs), MFMA busy share
+        assert cells[8] == "0.100"
+        assert cells[10] == "1.000"
+        assert cells[12] == "0.500"

@@ -10,7 +10,9 @@ This module turns one into the short text summaries kept under profiles/:
            scaled by what the same counter reads for a plain device copy of
            known size in the same run (`bench.py --copy-calibration`);
   ladder   the same for every rung of the ladder at both configured shapes
-           (bench.py run with its ladder), the points of the roofline chart.
+           (bench.py run with its ladder), the points of the roofline chart;
+  counters SQ instruction, LDS and MFMA counters of every rung from one
+           `--pmc` pass over bench.py's ladder.
 
 The traffic summary records a digest of the kernel sources; bench.py reports
 the stored traffic only while that digest matches the current sources.
@@ -151,10 +153,6 @@ def ladder_traffic(fetch_db, write_db):
     `--pmc` runs of bench.py with its ladder, keyed by (rung, workload).
     A rung's launch is recognised by its kernel name and its grid, which
     tra_gemm_describe gives for each configured shape."""
-    sys.path.insert(0, ROOT)
-    import tiling_roofline_analysis_amd as tra
-    from tiling_roofline_analysis_amd import inputs
-
     def rows(db):
         c = _db(db)
         return c.execute(
@@ -166,22 +164,94 @@ def ladder_traffic(fetch_db, write_db):
     cf = max((r for r in fr if COPY_KERNEL in r[0]), key=lambda r: r[1])
     cw = max((r for r in wr if COPY_KERNEL in r[0]), key=lambda r: r[1])
     fscale, wscale = COPY_BYTES / (cf[2] * 1024.0), COPY_BYTES / (cw[2] * 1024.0)
+    for rung, wname, kernel, lanes in ladder_launches():
+        f = [r for r in fr if _is_launch(r[0], r[1], kernel, lanes)]
+        wrow = [r for r in wr if _is_launch(r[0], r[1], kernel, lanes)]
+        if len(f) != 1 or len(wrow) != 1:
+            continue
+        out[(rung, wname)] = {
+            "kernel": kernel, "lanes": lanes, "dispatches": f[0][3],
+            "read_bytes": f[0][2] * 1024.0 * fscale, "write_bytes": wrow[0][2] * 1024.0 * wscale}
+    return out, fscale, wscale
+
+
+def ladder_launches():
+    """(rung, workload, kernel name, grid in lanes) of every launch that
+    bench.py's ladder makes, from tra_gemm_describe at both configured shapes."""
+    sys.path.insert(0, ROOT)
+    import tiling_roofline_analysis_amd as tra
+    from tiling_roofline_analysis_amd import inputs
     for wname in ("uniform1024", "normal4096"):
         w = inputs.WORKLOADS[wname]
         for v in tra.LADDER:
             d = tra.tra_gemm_describe(v, w.M, w.N, w.K)
             kv = dict(x.split("=", 1) for x in d.split() if "=" in x)
-            kernel = kv["kernel"].split("<")[0]
-            lanes = int(kv["grid"]) * int(kv["block"])
-            f = [r for r in fr if kernel + "<" in r[0] or kernel + "(" in r[0]]
-            f = [r for r in f if r[1] == lanes]
-            wrow = [r for r in wr if (kernel + "<" in r[0] or kernel + "(" in r[0]) and r[1] == lanes]
-            if len(f) != 1 or len(wrow) != 1:
-                continue
-            out[(tra.tra_gemm_variant_name(v), wname)] = {
-                "kernel": kernel, "lanes": lanes, "dispatches": f[0][3],
-                "read_bytes": f[0][2] * 1024.0 * fscale, "write_bytes": wrow[0][2] * 1024.0 * wscale}
-    return out, fscale, wscale
+            yield (tra.tra_gemm_variant_name(v), wname, kv["kernel"].split("<")[0],
+                   int(kv["grid"]) * int(kv["block"]))
+
+
+def _is_launch(name, grid, kernel, lanes):
+    return (kernel + "<" in name or kernel + "(" in name) and grid == lanes
+
+
+# Counters of one `--pmc` pass over bench.py's ladder (at most 8 SQ and 2 GRBM
+# counters fit in one pass).
+SQ_COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT",
+               "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_INST_LDS",
+               "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE")
+CUS, XCDS, SIMDS_PER_CU = 256, 8, 4
+
+
+def ladder_counters(db):
+    """Per-dispatch averages of SQ_COUNTERS for every rung of bench.py's
+    ladder, keyed by (rung, workload), plus the dispatch duration that the
+    same run recorded."""
+    c = _db(db)
+    rows = c.execute(
+        "select kernel_name, grid_size, counter_name, avg(value), count(*), avg(duration) "
+        "from counters_collection group by kernel_name, grid_size, counter_name").fetchall()
+    out = {}
+    for rung, wname, kernel, lanes in ladder_launches():
+        mine = [r for r in rows if _is_launch(r[0], r[1], kernel, lanes)]
+        if not mine or len({r[0] for r in mine}) != 1:
+            continue
+        d = {r[2]: r[3] for r in mine}
+        d["dispatches"] = mine[0][4]
+        d["duration_ns"] = mine[0][5]
+        d["kernel"] = kernel
+        out[(rung, wname)] = d
+    return out
+
+
+def counters_summary(db, cmd):
+    """Markdown table of the SQ counters per rung: what each rung of the
+    ladder spends its cycles on. GRBM_GUI_ACTIVE reads the sum over the XCDs;
+    divided by their count it is the kernel's length in GPU clocks, which the
+    summary checks against the recorded duration at 2.4 GHz."""
+    data = ladder_counters(db)
+    lines = [
+        "# SQ counters per launch of each rung (rocprofv3 --pmc)", "",
+        f"Command: `{cmd}`", "",
+        "Averages per dispatch. `clk` = GRBM_GUI_ACTIVE / 8 XCDs, the kernel's length in "
+        "GPU clocks (`clk / 2.4 GHz` is given beside the duration the same run recorded). "
+        "SIMD-clocks = 4 SIMDs x 256 CUs x clk.", "",
+        "| rung | workload | kernel | dispatches | duration us | clk/2.4GHz us | LDS instr | "
+        "bank-conflict cycles per LDS instr | LDS wait / wave cycles | VALU instr | "
+        "VALU instr per SIMD-clock | MFMA instr | MFMA busy / SIMD-clocks |",
+        "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for (rung, wname), d in data.items():
+        clk = d["GRBM_GUI_ACTIVE"] / XCDS
+        simd_clk = SIMDS_PER_CU * CUS * clk
+        lds = d["SQ_INSTS_LDS"]
+        conflict = d["SQ_LDS_BANK_CONFLICT"] / lds if lds else 0.0
+        wait = d["SQ_WAIT_INST_LDS"] / d["SQ_WAVE_CYCLES"] if d["SQ_WAVE_CYCLES"] else 0.0
+        lines.append(
+            f"| {rung} | {wname} | {d['kernel']} | {d['dispatches']} | "
+            f"{d['duration_ns'] / 1e3:.1f} | {clk / 2.4e3:.1f} | {lds:.4g} | {conflict:.3f} | "
+            f"{wait:.3f} | {d['SQ_INSTS_VALU']:.4g} | {d['SQ_INSTS_VALU'] / simd_clk:.3f} | "
+            f"{d['SQ_INSTS_MFMA']:.4g} | {d['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_clk:.3f} |")
+    lines += ["", f"sources_digest = {all_sources_digest()}"]
+    return "\n".join(lines) + "\n"
 
 
 def ladder_summary(fetch_db, write_db, cmd):
@@ -256,9 +326,14 @@ def main(argv=None):
     lad.add_argument("fetch_db")
     lad.add_argument("write_db")
     lad.add_argument("--cmd", required=True, help="profiling command with {counter}")
+    cnt = sub.add_parser("counters")
+    cnt.add_argument("db")
+    cnt.add_argument("--cmd", required=True, help="the profiling command")
     args = ap.parse_args(argv)
     if args.what == "trace":
         sys.stdout.write(trace_summary(args.db, args.cmd))
+    elif args.what == "counters":
+        sys.stdout.write(counters_summary(args.db, args.cmd))
     elif args.what == "ladder":
         sys.path.insert(0, ROOT)
         sys.stdout.write(ladder_summary(args.fetch_db, args.write_db, args.cmd))
