@@ -7,7 +7,8 @@ uniform[-1, 1) inputs (50 timed launches after warm-up, as the page "GEMM
 kernel test code & optimization (1024^3 experiment)" times its kernels);
 M = N = K = 4096 with normal(0, 1) inputs is reported beside it as
 "secondary".  Every rung of the kernel ladder is also timed on both shapes
-("ladder").
+("ladder"), and the library's own choice on the ragged and tall-skinny shapes
+and on one GPU's slab of the two large shapes split over 8 GPUs ("shapes").
 
 Timing: HIP events recorded on the stream the kernels are launched on
 (torch's current stream), around `--steps` back-to-back launches, after
@@ -33,6 +34,10 @@ sys.path.insert(0, ROOT)
 METRIC = "FP32 GEMM TFLOP/s and % of roofline at 1024³ and 4096³, 1× MI355X"
 PRIMARY = "uniform1024"
 SECONDARY = "normal4096"
+# Timed for context (`shapes` in the JSON line): the ragged and tall-skinny
+# shapes, and the per-GPU slabs of 4096^3 (512 rows of C) and of the
+# tall-skinny product (2048 of K) when split over 8 GPUs.
+OTHER_SHAPES = ("ragged", "tall", "rowslab4096", "kslab_tall")
 
 
 def log(*a):
@@ -194,6 +199,57 @@ def numpy_matmul(w):
     return {"ms": round(t * 1e3, 3), "tflops": round(w.flops / t / 1e12, 4)}
 
 
+def time_cold(tra, torch, w, dA, dB, dC, launches=20):
+    """Per-launch time with the caches flushed before each launch: a 512 MiB
+    buffer (twice the 256 MB last-level cache) is read and written between
+    launches, outside the event pair, so A and B come from HBM."""
+    stream = torch.cuda.current_stream()
+    handle = stream.cuda_stream
+    fn = tra.load().gemm_f32_variant
+    scratch = torch.zeros(128 << 20, dtype=torch.float32, device="cuda:0")
+    pairs = []
+    for _ in range(launches):
+        scratch.add_(1.0)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        st = fn(tra.AUTO, w.M, w.N, w.K, dA.data_ptr(), w.K, dB.data_ptr(), w.N,
+                dC.data_ptr(), w.N, handle)
+        if st != tra.TRA_OK:
+            raise tra.TraError(st, "gemm_f32_variant")
+        e1.record(stream)
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    del scratch
+    per = sorted(a.elapsed_time(b) for a, b in pairs[1:])
+    med = statistics.median(per)
+    return {"median_ms": round(med, 5), "min_ms": round(per[0], 5),
+            "tflops": round(w.flops / med / 1e9, 3), "launches": len(per)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_single_thread(w):
+    """One run of the CPU oracle on one thread: the other end of the oracle's
+    scaling, beside the all-core cpu_baseline."""
+    import oracle
+    A, B = w.make()
+    t0 = time.perf_counter()
+    oracle.gemm(A, B, nthreads=1)
+    t = time.perf_counter() - t0
+    return {"threads": 1, "seconds": round(t, 3), "gflops": round(w.flops / t / 1e9, 3),
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
+
+
 def cpu_baseline(w, seconds=10.0):
     """The CPU oracle on the full headline product, on the host's cores,
     repeated for about `seconds` of wall time (at least 3 runs); the median
@@ -230,6 +286,10 @@ def main():
     ap.add_argument("--warm-seconds", type=float, default=0.5,
                     help="untimed launches of the headline GEMM before its warm-up steps, so "
                          "the GPU runs at its sustained clocks when timing starts")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache timing of the two headline shapes")
+    ap.add_argument("--no-shapes", action="store_true",
+                    help="skip timing the ragged, tall-skinny and per-GPU-slab shapes")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip host-inclusive timing and the torch / numpy comparisons")
     ap.add_argument("--plot", metavar="SVG", help="write the roofline chart of the ladder here")
@@ -256,7 +316,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
 
-    def measure(name, steps, warmup, ladder):
+    def measure(name, steps, warmup, ladder, cold=False):
         w = inputs.WORKLOADS[name]
         A, B = w.make()
         dA = torch.from_numpy(A).to("cuda:0")
@@ -270,6 +330,9 @@ def main():
             f"median {med * 1e3:.2f}) = {rep['tflops']:.2f} TFLOP/s, "
             f"{100 * rep['frac_of_roof']:.1f}% of roof")
         out = {"w": w, "avg_ms": avg, "min_ms": mn, "median_ms": med, "rep": rep, "ladder": {}}
+        if cold:
+            out["cold"] = time_cold(tra, torch, w, dA, dB, dC)
+            log(f"[{name}] cold caches: {out['cold']}")
         if ladder:
             for v in tra.LADDER:
                 # keep each rung's timed region to about half a second
@@ -301,9 +364,23 @@ def main():
         torch.cuda.empty_cache()
 
     t_wall = time.perf_counter()
-    prim = measure(PRIMARY, args.steps, args.warmup, not args.no_ladder)
+    prim = measure(PRIMARY, args.steps, args.warmup, not args.no_ladder, not args.no_cold)
     sec = None if args.no_secondary else measure(SECONDARY, args.steps, args.warmup,
-                                                 not args.no_ladder)
+                                                 not args.no_ladder, not args.no_cold)
+    shapes = {}
+    if not args.no_shapes:
+        # Context beside the headline: the other large shapes and one GPU's
+        # share of the two large shapes split over 8 GPUs, each through AUTO.
+        for name in OTHER_SHAPES:
+            m = measure(name, args.steps, args.warmup, False)
+            ws, rep = m["w"], m["rep"]
+            shapes[name] = {
+                "workload": f"FP32 GEMM {ws.M}x{ws.N}x{ws.K} row-major, {ws.what}",
+                "value": round(rep["tflops"], 3), "unit": "TFLOP/s",
+                "ms_per_step": round(m["avg_ms"], 5), "min_ms": round(m["min_ms"], 5),
+                "frac_of_fp32_peak": round(rep["tflops"] / rl.PEAK_FP32_MFMA_TFLOPS, 4),
+                "frac_of_hbm_floor": round(rep["frac_of_hbm_floor"], 4),
+                "kernel": tra.tra_gemm_describe(tra.AUTO, ws.M, ws.N, ws.K)}
     gpu_wall = time.perf_counter() - t_wall
     roofs = None
     if not args.no_roofs:
@@ -349,6 +426,10 @@ def main():
             "measured_roofs": roofs,
         },
     }
+    if "cold" in prim:
+        line["detail"]["cold"] = {PRIMARY: prim["cold"]}
+        if sec is not None:
+            line["detail"]["cold"][SECONDARY] = sec["cold"]
     if prim["ladder"]:
         line["ladder"] = {PRIMARY: prim["ladder"]}
     if sec is not None:
@@ -362,6 +443,8 @@ def main():
         }
         if sec["ladder"]:
             line.setdefault("ladder", {})[SECONDARY] = sec["ladder"]
+    if shapes:
+        line["shapes"] = shapes
     if not args.no_compare:
         comp = {}
         for name in (PRIMARY,) + (() if args.no_secondary else (SECONDARY,)):
@@ -380,6 +463,8 @@ def main():
         log("[cpu_baseline] timing the oracle ...")
         line["cpu_baseline"] = cpu_baseline(inputs.WORKLOADS[PRIMARY])
         log(f"[cpu_baseline] {line['cpu_baseline']['value'] * 1e3:.3f} GFLOP/s")
+        line["detail"]["cpu_oracle_1thread"] = cpu_single_thread(inputs.WORKLOADS[PRIMARY])
+        log(f"[cpu_baseline] one thread: {line['detail']['cpu_oracle_1thread']}")
     print(json.dumps(line), flush=True)
 
 

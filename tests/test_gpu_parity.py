@@ -162,7 +162,12 @@ def sample_entries(M, N, seed, n_random=20000):
     return np.concatenate(rs), np.concatenate(cs)
 
 
-@pytest.mark.parametrize("name", ["normal4096", "ragged", "tall"])
+# the configured large shapes, and one GPU's slab of the two largest split
+# over 8 GPUs (512 rows of 4096^3; 2048 of the tall-skinny K)
+LARGE = ["normal4096", "ragged", "tall", "rowslab4096", "kslab_tall"]
+
+
+@pytest.mark.parametrize("name", LARGE)
 @pytest.mark.parametrize("variant", RUNGS, ids=RUNG_IDS)
 def test_large_configs_sampled(variant, name):
     w = inputs.WORKLOADS[name]
@@ -176,7 +181,7 @@ def test_large_configs_sampled(variant, name):
     assert np.isfinite(C).all()
 
 
-@pytest.mark.parametrize("name", ["normal4096", "ragged", "tall"])
+@pytest.mark.parametrize("name", LARGE)
 @pytest.mark.parametrize("variant", RUNGS, ids=RUNG_IDS)
 def test_large_shapes_int_patterns_every_element(variant, name):
     w = inputs.WORKLOADS[name]

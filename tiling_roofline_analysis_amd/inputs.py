@@ -136,5 +136,11 @@ WORKLOADS = {
                  "3000x2049x1531, uniform[-1,1) seeds 3000/3001"),
         Workload("tall", 16384, 64, 16384, "uniform", 16384,
                  "16384x64x16384 tall-skinny, uniform[-1,1) seeds 16384/16385"),
+        # One GPU's share when the two large shapes are split over 8 GPUs:
+        # a slab of 512 rows of C (all of K and N), and a slab of 2048 of K.
+        Workload("rowslab4096", 512, 4096, 4096, "normal", 4096,
+                 "512x4096x4096 row slab (4096^3 over 8 GPUs), normal(0,1) seeds 4096/4097"),
+        Workload("kslab_tall", 16384, 64, 2048, "uniform", 16384,
+                 "16384x64x2048 K slab (tall-skinny over 8 GPUs), uniform[-1,1) seeds 16384/16385"),
     ]
 }

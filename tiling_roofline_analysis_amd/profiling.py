@@ -84,6 +84,29 @@ def _db(path):
     return sqlite3.connect(f"file:{path}?mode=ro", uri=True)
 
 
+def _short(name):
+    return name.replace("(anonymous namespace)::", "").split("(long")[0]
+
+
+def trace_series(db: str, min_dispatches: int = 10):
+    """Maximal runs of consecutive dispatches (in start order) of one kernel
+    at one grid, with at least `min_dispatches` dispatches: the series that a
+    benchmark times back to back.  Two shapes that launch the same kernel
+    with the same grid stay apart here, where a grouping by name and grid
+    would average them together."""
+    c = _db(db)
+    rows = c.execute(
+        "select name, grid_x*grid_y*grid_z, workgroup_x*workgroup_y*workgroup_z, duration "
+        "from kernels order by start").fetchall()
+    runs = []
+    for name, grid, wg, dur in rows:
+        if runs and runs[-1]["name"] == name and runs[-1]["grid"] == grid:
+            runs[-1]["d"].append(dur)
+        else:
+            runs.append({"name": name, "grid": grid, "block": wg, "d": [dur]})
+    return [r for r in runs if len(r["d"]) >= min_dispatches]
+
+
 def trace_summary(db: str, cmd: str) -> str:
     c = _db(db)
     rows = c.execute(
@@ -92,12 +115,23 @@ def trace_summary(db: str, cmd: str) -> str:
         "group by name, grid_x, grid_y, grid_z order by sum(duration) desc").fetchall()
     out = [f"# rocprofv3 kernel trace summary", "",
            f"command: `{cmd}`", "",
-           "| kernel | grid (lanes) | block | dispatches | avg us | min us | max us |",
-           "|---|---|---|---|---|---|---|"]
+           "## Series of back-to-back dispatches, in launch order", "",
+           "Each row is a maximal run of consecutive dispatches of one kernel at one grid "
+           "(at least 10): a timed series of the benchmark.", "",
+           "| # | kernel | grid (lanes) | block | dispatches | avg us | median us | min us | max us |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for i, r in enumerate(trace_series(db)):
+        d = sorted(r["d"])
+        med = d[len(d) // 2] if len(d) % 2 else 0.5 * (d[len(d) // 2 - 1] + d[len(d) // 2])
+        out.append(f"| {i} | `{_short(r['name'])}` | {r['grid']} | {r['block']} | {len(d)} | "
+                   f"{sum(d) / len(d) / 1e3:.2f} | {med / 1e3:.2f} | {d[0] / 1e3:.2f} | "
+                   f"{d[-1] / 1e3:.2f} |")
+    out += ["", "## All dispatches by kernel and grid", "",
+            "| kernel | grid (lanes) | block | dispatches | avg us | min us | max us |",
+            "|---|---|---|---|---|---|---|"]
     for name, grid, wg, n, avg, mn, mx, _ in rows:
-        short = name.replace("(anonymous namespace)::", "").split("(long")[0]
-        out.append(f"| `{short}` | {grid} | {wg} | {n} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | "
-                   f"{mx / 1e3:.2f} |")
+        out.append(f"| `{_short(name)}` | {grid} | {wg} | {n} | {avg / 1e3:.2f} | "
+                   f"{mn / 1e3:.2f} | {mx / 1e3:.2f} |")
     return "\n".join(out) + "\n"
 
 
