@@ -36,22 +36,49 @@ def test_ladder_launches_cover_every_rung_at_both_shapes():
         assert w.M * w.N > 0
 
 
-def test_trace_summary(tmp_path):
-    db = tmp_path / "t.db"
-    c = sqlite3.connect(db)
+def _trace_db(path, rows):
+    c = sqlite3.connect(path)
     c.execute("create table kernels (name text, grid_x int, grid_y int, grid_z int, "
-              "workgroup_x int, workgroup_y int, workgroup_z int, duration real)")
-    c.executemany("insert into kernels values (?,?,?,?,?,?,?,?)",
-                  [("k1(long)", 256, 1, 1, 256, 1, 1, d) for d in (1000.0, 3000.0)]
-                  + [("k2(long)", 64, 1, 1, 64, 1, 1, 500.0)])
+              "workgroup_x int, workgroup_y int, workgroup_z int, start int, duration real)")
+    c.executemany("insert into kernels values (?,?,?,?,?,?,?,?,?)", rows)
     c.commit()
     c.close()
+
+
+def test_trace_summary(tmp_path):
+    db = tmp_path / "t.db"
+    _trace_db(db, [("k1(long)", 256, 1, 1, 256, 1, 1, t, d)
+                   for t, d in ((0, 1000.0), (5000, 3000.0))]
+              + [("k2(long)", 64, 1, 1, 64, 1, 1, 9000, 500.0)])
     text = profiling.trace_summary(str(db), "cmd")
-    line = [x for x in text.splitlines() if "`k1`" in x][0]
+    by_kernel = text.split("## All dispatches")[1]
+    line = [x for x in by_kernel.splitlines() if "`k1`" in x][0]
     cells = [x.strip() for x in line.strip("|").split("|")]
     assert cells[1:] == ["256", "256", "2", "2.00", "1.00", "3.00"]
     # ordered by total time: k1 (4 us) before k2 (0.5 us)
-    assert text.index("`k1`") < text.index("`k2`")
+    assert by_kernel.index("`k1`") < by_kernel.index("`k2`")
+
+
+def test_trace_series_split_one_kernel_between_two_shapes(tmp_path):
+    # one kernel at one grid in two timed series with another kernel between
+    # them (two shapes that share a tile class): the series stay apart
+    db = tmp_path / "s.db"
+    rows, t = [], 0
+    for dur, n in ((20_000.0, 30), (40_000.0, 12)):
+        for _ in range(n):
+            rows.append(("gemm(long)", 65536, 1, 1, 256, 1, 1, t, dur))
+            t += 100_000
+        rows.append(("other(long)", 64, 1, 1, 64, 1, 1, t, 1.0))
+        t += 100_000
+    rows.append(("gemm(long)", 65536, 1, 1, 256, 1, 1, t, 1e6))   # a lone dispatch
+    _trace_db(db, rows)
+    series = profiling.trace_series(str(db))
+    assert [len(r["d"]) for r in series] == [30, 12]
+    assert [sum(r["d"]) / len(r["d"]) for r in series] == [20_000.0, 40_000.0]
+    text = profiling.trace_summary(str(db), "cmd")
+    first = text.split("## All dispatches")[0]
+    assert "| 0 | `gemm` | 65536 | 256 | 30 | 20.00 | 20.00 | 20.00 | 20.00 |" in first
+    assert "| 1 | `gemm` | 65536 | 256 | 12 | 40.00 |" in first
 
 
 def test_ladder_traffic_scales_by_the_copy(tmp_path):
