@@ -216,6 +216,10 @@ def test_caller_workspace_checked_on_host():
     ((300, 500, 203), "mfma"),             # 40 tiles of 7 slices: too short to share
     ((100, 100, 300), "mfma"),             # 4 tiles of 10 slices: saves < 8 us
     ((100, 100, 2000), "mfma_streamk"),    # 4 tiles of 63 slices
+    ((8192, 64, 2048), "mfma_streamk"),    # 128 tiles: exactly half the CUs
+    ((4096, 128, 2048), "mfma_streamk"),   # 128 tiles
+    ((12288, 64, 2048), "mfma"),           # 192 tiles, 2 GFLOP: too small to split
+    ((768, 768, 1024), "mfma"),            # 144 tiles of 32 slices
 ])
 def test_auto_choice(shape, rung):
     d = tra.tra_gemm_describe(tra.AUTO, *shape)

@@ -777,10 +777,11 @@ LaunchPlan plan_mfma(int64_t M, int64_t N, int64_t K, bool stream_k) {
 
 // AUTO's choice, from timings of both forms on MI355X.  The split needs K
 // to have at least 8 slices to share out, and then pays
-//   * when fewer tiles than half the CUs would leave most CUs idle and the
-//     time that sharing saves -- (1 - tiles/CUs) of one tile's slices at
-//     the measured per-CU MFMA rate (148 TFLOP/s over 256 CUs) -- covers
-//     the second launch (8 us; 200x300x4100: 20 tiles, 67 -> ~20 us);
+//   * when at most half the CUs would have a tile and the time that
+//     sharing saves -- (1 - tiles/CUs) of one tile's slices at the
+//     measured per-CU MFMA rate (148 TFLOP/s over 256 CUs) -- covers the
+//     second launch (8 us; 200x300x4100: 20 tiles, 67 -> ~20 us; exactly
+//     half, 8192x64x2048: 128 tiles, 37 -> 29 us);
 //   * otherwise when one tile per workgroup would leave some CUs a whole
 //     tile more work than the mean (at least 10% more: e.g. 1296 tiles on
 //     256 CUs, 5.06 a CU, so some CUs run 6) and the product is large
@@ -792,7 +793,7 @@ bool stream_k_pays(int64_t M, int64_t N, int64_t K) {
     if (p.sk_tiles == 0 || p.ipt < 8) return false;
     const int64_t cus = device_cus();
     const int64_t tiles = static_cast<int64_t>(p.tiles_m) * p.tiles_n;
-    if (2 * tiles < cus) {
+    if (2 * tiles <= cus) {
         const double slice_s = 2.0 * T::BM * T::BN * T::BK / (148e12 / 256);
         const double saved = (1.0 - static_cast<double>(tiles) / static_cast<double>(cus)) *
                              static_cast<double>(p.ipt) * slice_s;
