@@ -56,13 +56,13 @@ def test_describe_plans():
     assert "gemm_mfma_f32" in d and "tile=256x128x16" in d and "grid=512" in d
     assert "block=512" in d
     d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 1024)
-    assert "tile=64x64x32" in d and "grid=256" in d and "block=256" in d
+    assert "tile=64x64x16" in d and "4 sets" not in d and "grid=256" in d and "block=256" in d
     d = tra.tra_gemm_describe(tra.MFMA, 2048, 2048, 2048)
     assert "tile=128x128x16" in d and "8 waves" in d and "grid=256" in d and "block=512" in d
     d = tra.tra_gemm_describe(tra.MFMA, 16384, 64, 16384)
-    assert "tile=64x64x32" in d and "4 sets" in d and "grid=256" in d
+    assert "tile=64x64x16" in d and "4 sets" in d and "grid=256" in d
     d = tra.tra_gemm_describe(tra.MFMA, 3000, 2049, 1531)
-    assert "tile=64x64x32" in d and "grid=1551" in d and "block=256" in d
+    assert "tile=64x64x16" in d and "4 sets" in d and "grid=1551" in d and "block=256" in d
     d = tra.tra_gemm_describe(tra.NAIVE, 1024, 1024, 1024)
     assert "gemm_naive_f32" in d and "grid=4096" in d and "block=256" in d
     d = tra.tra_gemm_describe(tra.LDS_TILED, 1024, 1024, 1024)
@@ -71,7 +71,7 @@ def test_describe_plans():
     assert "grid=408" in d   # 24 x 17 tiles of 128 x 128
     assert tra.tra_gemm_describe(tra.AUTO, 16, 16, 16).startswith("variant=auto")
     # stream-K: 1551 tiles of 64 x 64 on 256 CUs x 2 workgroups leave a last
-    # wave of 15 tiles; their 15 x 48 slices go to 120 workgroups of 6 (an
+    # wave of 15 tiles; their 15 x 96 slices go to 120 workgroups of 12 (an
     # eighth of a tile each), with two partial tiles of 16 KiB per
     # workgroup; the main launch adds 4 fixup chunks per shared tile
     d = tra.tra_gemm_describe(tra.MFMA_STREAMK, 3000, 2049, 1531)
@@ -80,10 +80,10 @@ def test_describe_plans():
     # whole waves of tiles: no split, no workspace
     d = tra.tra_gemm_describe(tra.MFMA_STREAMK, 4096, 4096, 4096)
     assert "stream_k_tiles=0" in d and "workspace_bytes=0" in d
-    # fewer tiles than a wave: all of them split (40 tiles x 7 slices of 32
-    # over 140 workgroups of at least 2 slices)
+    # fewer tiles than a wave: all of them split (40 tiles x 13 slices of 16
+    # over 260 workgroups of at least 2 slices)
     d = tra.tra_gemm_describe(tra.MFMA_STREAMK, 300, 500, 203)
-    assert "stream_k_tiles=40" in d and "stream_k_wgs=140" in d
+    assert "stream_k_tiles=40" in d and "stream_k_wgs=260" in d
     assert "stream_k_tiles=0" in tra.tra_gemm_describe(tra.MFMA, 3000, 2049, 1531)
     with pytest.raises(tra.TraError):
         tra.tra_gemm_describe(7, 1, 1, 1)
@@ -173,8 +173,8 @@ def test_workspace_size():
     assert tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, 3000, 2049, 1531) == 2 * 120 * 64 * 64 * 4
     assert tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, 4096, 4096, 4096) == 0
     assert tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, 0, 2049, 1531) == 0
-    # K of one slice leaves nothing to split
-    assert tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, 3000, 2049, 32) == 0
+    # K of one slice (16 deep) leaves nothing to split
+    assert tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, 3000, 2049, 16) == 0
     for bad in [(6, 1, 1, 1), (tra.MFMA, -1, 1, 1), (tra.MFMA, 1, 1, -1)]:
         with pytest.raises(tra.TraError):
             tra.tra_gemm_workspace_size(*bad)

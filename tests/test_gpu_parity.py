@@ -229,9 +229,10 @@ def test_edge_sizes(variant):
 MFMA_TILE_SHAPES = [
     (4000, 4200, 203, "<256x128x16, 8 waves>"),   # 16 x 33 = 528 tiles of 256 x 128
     (1900, 2000, 300, "<128x128x16, 8 waves>"),   # 15 x 16 = 240 tiles of 128 x 128
-    (1500, 1500, 77, "<64x64x32, 4 waves>"),      # 576 tiles of 64 x 64, short K
-    (200, 300, 4100, "<64x64x32, 4 waves, 4 sets>"),   # few tiles, long K
-    (300, 500, 203, "<64x64x32, 4 waves>"),       # few tiles
+    (1500, 1500, 77, "<64x64x16, 4 waves>"),      # 576 tiles of 64 x 64, short K
+    (200, 300, 4100, "<64x64x16, 4 waves, 4 sets>"),   # few tiles, long K
+    (300, 500, 203, "<64x64x16, 4 waves>"),       # few tiles
+    (700, 900, 1500, "<64x64x16, 4 waves, 4 sets>"),   # 165 tiles, K > 1024
 ]
 
 
