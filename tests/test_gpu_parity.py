@@ -227,7 +227,7 @@ def test_edge_sizes(variant):
 # Shapes that send the MFMA rung to each of its tile shapes, with tails on
 # every axis: (M, N, K, expected tile).
 MFMA_TILE_SHAPES = [
-    (4000, 4200, 203, "<256x128x16, 8 waves>"),   # 16 x 33 = 528 tiles of 256 x 128
+    (4000, 4200, 203, "<256x128x16, 8 waves, 4 sets>"),   # 16 x 33 = 528 tiles of 256 x 128
     (1900, 2000, 300, "<128x128x16, 8 waves>"),   # 15 x 16 = 240 tiles of 128 x 128
     (1500, 1500, 77, "<64x64x16, 4 waves>"),      # 576 tiles of 64 x 64, short K
     (200, 300, 4100, "<64x64x16, 4 waves, 4 sets>"),   # few tiles, long K

@@ -652,8 +652,8 @@ void gemm_mfma_f32_sk(int64_t M, int64_t N, int64_t K,
 
 // Tile shapes (chosen by timing candidates on MI355X, interleaved and
 // repeated on one warm GPU):
-//   Large  256x128x16, 8 waves of 64x64, two register sets: shapes with at
-//          least 4 tiles of 128x128 per CU (4096^3: 512 such tiles).
+//   Large  256x128x16, 8 waves of 64x64, four register sets: shapes with
+//          at least 4 tiles of 128x128 per CU (4096^3: 512 such tiles).
 //   Mid    128x128x16, 8 waves of 64x32: about one 128x128 tile per CU
 //          (2048^3: 256 tiles).
 //   Many   64x64x16, 4 waves of 32x32, two register sets: every other
@@ -663,7 +663,7 @@ void gemm_mfma_f32_sk(int64_t M, int64_t N, int64_t K,
 // With the loop's waits exact (see k_loop), the 16-deep slices of the Many
 // and Deep tiles beat 32-deep ones by 1-2.5% on most shapes, and need 124
 // VGPRs instead of about 200.
-using TileLarge = MfmaTile<256, 128, 16, 64, 64, 2>;
+using TileLarge = MfmaTile<256, 128, 16, 64, 64, 4>;
 using TileMid = MfmaTile<128, 128, 16, 64, 32, 2>;
 using TileMany = MfmaTile<64, 64, 16, 32, 32, 2>;
 using TileDeep = MfmaTile<64, 64, 16, 32, 32, 4>;
@@ -803,7 +803,8 @@ hipError_t launch_tile(const GemmArgs &a, bool stream_k, void *ws, size_t ws_byt
 LaunchPlan plan_mfma(int64_t M, int64_t N, int64_t K, bool stream_k) {
     switch (pick(M, N, K)) {
         case Shape::kLarge:
-            return plan_for<TileLarge>(M, N, K, stream_k, "gemm_mfma_f32<256x128x16, 8 waves>");
+            return plan_for<TileLarge>(M, N, K, stream_k,
+                                       "gemm_mfma_f32<256x128x16, 8 waves, 4 sets>");
         case Shape::kMid:
             return plan_for<TileMid>(M, N, K, stream_k, "gemm_mfma_f32<128x128x16, 8 waves>");
         case Shape::kMany:
