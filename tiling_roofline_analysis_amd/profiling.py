@@ -132,6 +132,15 @@ def trace_summary(db: str, cmd: str) -> str:
     for name, grid, wg, n, avg, mn, mx, _ in rows:
         out.append(f"| `{_short(name)}` | {grid} | {wg} | {n} | {avg / 1e3:.2f} | "
                    f"{mn / 1e3:.2f} | {mx / 1e3:.2f} |")
+    has_stats = c.execute("select count(*) from sqlite_master where name = 'top_kernels'").fetchone()[0]
+    if has_stats:
+        # rocprofv3's own --stats summary (by kernel name over all grids), as it wrote it
+        out += ["", "## rocprofv3 --stats (its `top_kernels` table, by kernel name)", "",
+                "| kernel | calls | total us | average us | % of kernel time |", "|---|---|---|---|---|"]
+        for name, calls, total, avg, pct in c.execute(
+                "select name, total_calls, total_duration, average, percentage from top_kernels"):
+            out.append(f"| `{_short(name)}` | {calls} | {float(total):.1f} | {float(avg):.3f} | "
+                       f"{float(pct):.2f} |")
     return "\n".join(out) + "\n"
 
 
