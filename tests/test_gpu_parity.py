@@ -224,6 +224,24 @@ def test_edge_sizes(variant):
                 assert_exact(Ci, refi.c32, f"small ints {M}x{N}x{K}")
 
 
+# Every (M, N) pair of the tile-edge sizes, with K running through the same
+# sizes, so that each size appears on each axis next to every other size.
+EDGE_ALL = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 257]
+
+
+@pytest.mark.parametrize("variant", RUNGS + [tra.AUTO], ids=RUNG_IDS + ["auto"])
+def test_edge_sizes_all_pairs(variant):
+    n = len(EDGE_ALL)
+    for i, M in enumerate(EDGE_ALL):
+        for j, N in enumerate(EDGE_ALL):
+            K = EDGE_ALL[(i + 3 * j) % n]
+            Ai = inputs.small_ints(M, K, 7 * M + K)
+            Bi = inputs.small_ints(K, N, 11 * N + K)
+            refi = oracle.gemm(Ai, Bi)
+            Ci, *_ = run_gpu(variant, Ai, Bi)
+            assert_exact(Ci, refi.c32, f"small ints {M}x{N}x{K}")
+
+
 # Shapes that send the MFMA rung to each of its tile shapes, with tails on
 # every axis: (M, N, K, expected tile).
 MFMA_TILE_SHAPES = [
