@@ -26,8 +26,8 @@
 //             in 4 disjoint bank groups; global float4 rows store as-is.
 //   Bs[k][n]  n contiguous, row stride 132 words: a wave reads 64
 //             consecutive words per ds_read_b128.
-// The arithmetic is VALU fmaf (v_fma_f32); packed-FP32 instructions are
-// disabled for this build, so the rung's ceiling is the unpacked FP32 VALU
+// The arithmetic is VALU fmaf (v_fma_f32); the library is compiled with
+// packed-FP32 instructions disabled, so the rung's ceiling is the unpacked FP32 VALU
 // rate (about 100 TFLOP/s measured by tra_probe_fma_f32 on MI355X), below
 // the 157.3 TFLOP/s FP32 peak that the matrix cores reach.
 #include "gemm_internal.h"

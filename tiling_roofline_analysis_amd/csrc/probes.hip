@@ -11,7 +11,7 @@
 //   * mfma  -- back-to-back independent v_mfma_f32_32x32x2_f32 from
 //              registers: the FP32 matrix-core roof;
 //   * fma   -- independent v_fma_f32 chains from registers: the FP32 VALU
-//              roof of this build (no packed-FP32 instructions).
+//              roof of code compiled without packed-FP32 instructions.
 // Each compute probe writes one value per lane to a sink so nothing is
 // optimised away; results are meaningless numbers.
 #include <algorithm>
