@@ -68,7 +68,11 @@ def test_describe_plans():
     d = tra.tra_gemm_describe(tra.LDS_TILED, 1024, 1024, 1024)
     assert "tile=32x32x32" in d and "block=1024" in d
     d = tra.tra_gemm_describe(tra.REGBLOCK_DB, 3000, 2049, 1531)
-    assert "grid=408" in d   # 24 x 17 tiles of 128 x 128
+    assert "grid=1551" in d and "64x64" in d    # 408 tiles of 128 x 128 are too few
+    d = tra.tra_gemm_describe(tra.REGBLOCK_DB, 4096, 4096, 4096)
+    assert "grid=1024" in d and "128x128" in d  # 4 tiles of 128 x 128 a CU
+    d = tra.tra_gemm_describe(tra.REGBLOCK_DB, 3072, 3072, 3072)
+    assert "grid=2304" in d and "64x64" in d    # 576 large tiles: 2.25 a CU
     assert tra.tra_gemm_describe(tra.AUTO, 16, 16, 16).startswith("variant=auto")
     # stream-K: 1551 tiles of 64 x 64 on 256 CUs x 2 workgroups leave a last
     # wave of 15 tiles; their 15 x 96 slices go to 120 workgroups of 12 (an

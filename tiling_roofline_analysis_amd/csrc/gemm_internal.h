@@ -90,4 +90,68 @@ __device__ __forceinline__ void grouped_tile(int64_t id, int64_t tiles_m, int64_
     tn = in / rows;
 }
 
+// ---- operand loads and tile placement shared by the tiled rungs ----
+
+// X[row][col .. col+3] of a rows x cols row-major matrix, zero outside it.
+// Addresses are clamped into the matrix, so every load is valid, and the
+// zero is applied with an AND mask on the loaded bits: the loads are
+// unconditional (a select would let the compiler predicate each load behind
+// a branch and wait for it).
+__device__ __forceinline__ float4 load4_clamped(const float *X, int64_t ld, int64_t row,
+                                                int64_t col, int64_t rows, int64_t cols) {
+    const bool rok = row < rows;
+    const float *p = X + (rok ? row : rows - 1) * ld;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t c = col + e;
+        const float x = p[c < cols ? c : cols - 1];
+        const unsigned keep = (rok && c < cols) ? 0xffffffffu : 0u;
+        v[e] = __uint_as_float(__float_as_uint(x) & keep);
+    }
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// How a slice is loaded from global memory.  A tile is always placed
+// inside the matrices when they are at least one tile large (see
+// tile_origin below), so only the slice that runs past K and matrices
+// smaller than a tile need index checks.
+//   kVec      A and B rows 16-byte aligned at the tile: float4 loads;
+//   kVecA     A aligned, B not (ldb or the tile's first column not a
+//             multiple of 4): float4 loads of A, element loads of B;
+//   kScalar   element loads of both;
+//   kChecked  element loads at clamped addresses with zeros outside the
+//             matrices (the k tail slice, and tiles larger than the matrix).
+enum LoadMode { kVec = 0, kVecA = 1, kScalar = 2, kChecked = 3 };
+
+__device__ __forceinline__ float4 load4_scalar(const float *p) {
+    return make_float4(p[0], p[1], p[2], p[3]);
+}
+
+// Where block tile (tm, tn) sits.  A tile that would cross row M (column
+// N) of a matrix at least BM rows (BN columns) large is moved back to end at
+// row M (column N), so every load of a full slice stays inside the
+// matrices with no checks; its first skip_m rows (skip_n columns) belong to
+// the tile before it and are not stored.  Only matrices smaller than a tile
+// leave tiles that hang over an edge (loaded with checks).
+struct Origin {
+    int64_t m0, n0;
+    int skip_m, skip_n;
+};
+
+template <int BM, int BN>
+__host__ __device__ __forceinline__ Origin tile_origin(int64_t tm, int64_t tn, int64_t M,
+                                                       int64_t N) {
+    Origin o{tm * BM, tn * BN, 0, 0};
+    if (o.m0 + BM > M && M >= BM) {
+        o.skip_m = static_cast<int>(o.m0 + BM - M);
+        o.m0 = M - BM;
+    }
+    if (o.n0 + BN > N && N >= BN) {
+        o.skip_n = static_cast<int>(o.n0 + BN - N);
+        o.n0 = N - BN;
+    }
+    return o;
+}
+
 }  // namespace tra

@@ -91,26 +91,6 @@ struct MfmaTile {
     static_assert(NR == 1 || NR == 2 || NR == 4, "1, 2 or 4 register sets");
 };
 
-// X[row][col .. col+3] of a rows x cols row-major matrix, zero outside it.
-// Addresses are clamped into the matrix, so every load is valid, and the
-// zero is applied with an AND mask on the loaded bits: the loads are
-// unconditional (a select would let the compiler predicate each load behind
-// a branch and wait for it).
-__device__ __forceinline__ float4 load4_clamped(const float *X, int64_t ld, int64_t row,
-                                                int64_t col, int64_t rows, int64_t cols) {
-    const bool rok = row < rows;
-    const float *p = X + (rok ? row : rows - 1) * ld;
-    float v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int64_t c = col + e;
-        const float x = p[c < cols ? c : cols - 1];
-        const unsigned keep = (rok && c < cols) ? 0xffffffffu : 0u;
-        v[e] = __uint_as_float(__float_as_uint(x) & keep);
-    }
-    return make_float4(v[0], v[1], v[2], v[3]);
-}
-
 template <class T>
 struct Ctx {
     int64_t M, N, K;
@@ -121,22 +101,6 @@ struct Ctx {
     int64_t m0, n0;
     int t;
 };
-
-// How a slice is loaded from global memory.  A tile is always placed inside
-// the matrices when they are at least one tile large (see tile_origin), so
-// only the slice that runs past K and matrices smaller than a tile need
-// index checks.
-//   kVec      A and B rows 16-byte aligned at the tile: float4 loads;
-//   kVecA     A aligned, B not (ldb or the tile's first column not a
-//             multiple of 4): float4 loads of A, element loads of B;
-//   kScalar   element loads of both;
-//   kChecked  element loads at clamped addresses with zeros outside the
-//             matrices (the k tail slice, and tiles larger than the matrix).
-enum LoadMode { kVec = 0, kVecA = 1, kScalar = 2, kChecked = 3 };
-
-__device__ __forceinline__ float4 load4_scalar(const float *p) {
-    return make_float4(p[0], p[1], p[2], p[3]);
-}
 
 // Loads slice k0 .. k0+BK of the A and B tiles into registers.
 template <class T, int MODE>
@@ -417,32 +381,6 @@ __host__ __device__ __forceinline__ int sk_owner(const SkPlan &p, int it) {
 // Workspace slot of the partial sum of tile `tile` by stream-K workgroup w.
 __host__ __device__ __forceinline__ int sk_slot(const SkPlan &p, int w, int tile) {
     return 2 * w + (tile == sk_begin(p, w) / static_cast<int>(p.ipt) ? 0 : 1);
-}
-
-// Where block tile (tm, tn) sits.  A tile that would cross row M (column
-// N) of a matrix at least BM rows (BN columns) large is moved back to end at
-// row M (column N), so every load of a full slice stays inside the
-// matrices with no checks; its first skip_m rows (skip_n columns) belong to
-// the tile before it and are not stored.  Only matrices smaller than a tile
-// leave tiles that hang over an edge (loaded with checks).
-struct Origin {
-    int64_t m0, n0;
-    int skip_m, skip_n;
-};
-
-template <int BM, int BN>
-__host__ __device__ __forceinline__ Origin tile_origin(int64_t tm, int64_t tn, int64_t M,
-                                                       int64_t N) {
-    Origin o{tm * BM, tn * BN, 0, 0};
-    if (o.m0 + BM > M && M >= BM) {
-        o.skip_m = static_cast<int>(o.m0 + BM - M);
-        o.m0 = M - BM;
-    }
-    if (o.n0 + BN > N && N >= BN) {
-        o.skip_n = static_cast<int>(o.n0 + BN - N);
-        o.n0 = N - BN;
-    }
-    return o;
 }
 
 // One pass of the block tile at (c.m0, c.n0) over slices s0 .. s0+n-1

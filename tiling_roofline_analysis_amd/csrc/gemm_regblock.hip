@@ -10,12 +10,17 @@
 // "GEMM kernel test code & optimization (1024^3 experiment)", section
 // "Key idea: reuse through shared memory").  This rung pushes both levers:
 //   * a 128 x 128 block tile of C (each staged element reused 128 times;
-//     64 x 64 when 128 x 128 tiles would not give every CU one);
+//     64 x 64 when there are too few 128 x 128 tiles to give every CU two,
+//     or they split unevenly over the CUs);
 //   * each lane holds an 8 x 8 (4 x 4) micro-tile of C in VGPRs, so one LDS
 //     read feeds 8 (4) FMAs instead of one;
 //   * the next K slice is fetched into registers while the current one is
 //     consumed from LDS, and two LDS buffers alternate, so each slice needs
-//     one barrier instead of two.
+//     one barrier instead of two;
+//   * a tile at the bottom or right edge is moved back inside the matrix
+//     (tile_origin), so full slices load with no bounds checks; only the
+//     slice that runs past K, and matrices smaller than a tile, load with
+//     checks.
 //
 // gfx950 layout (256 lanes = 4 wave64s, lane t: tx = t % 16, ty = t / 16),
 // for the 128 x 128 tile (the 64 x 64 one keeps i < 4 and the first group):
@@ -27,9 +32,9 @@
 //   Bs[k][n]  n contiguous, row stride 132 words: a wave reads 64
 //             consecutive words per ds_read_b128.
 // The arithmetic is VALU fmaf (v_fma_f32); the library is compiled with
-// packed-FP32 instructions disabled, so the rung's ceiling is the unpacked FP32 VALU
-// rate (about 100 TFLOP/s measured by tra_probe_fma_f32 on MI355X), below
-// the 157.3 TFLOP/s FP32 peak that the matrix cores reach.
+// packed-FP32 instructions disabled, so the rung's ceiling is the unpacked
+// FP32 VALU rate (about 100 TFLOP/s measured by tra_probe_fma_f32 on
+// MI355X), below the 157.3 TFLOP/s FP32 peak that the matrix cores reach.
 #include "gemm_internal.h"
 
 namespace tra {
@@ -51,17 +56,135 @@ struct RegTile {
     static_assert(AF4 >= 1 && BF4 >= 1, "whole float4 per lane");
 };
 
-// Loads 4 consecutive floats p[0..3] of a row; elements at or past `lim`
-// (or the whole group when !row_ok) read as zero.
-__device__ __forceinline__ float4 load4(const float *p, bool row_ok, int64_t first,
-                                        int64_t lim, bool vec) {
-    if (row_ok && vec && first + 3 < lim) return *reinterpret_cast<const float4 *>(p);
-    float4 v;
-    v.x = (row_ok && first + 0 < lim) ? p[0] : 0.0f;
-    v.y = (row_ok && first + 1 < lim) ? p[1] : 0.0f;
-    v.z = (row_ok && first + 2 < lim) ? p[2] : 0.0f;
-    v.w = (row_ok && first + 3 < lim) ? p[3] : 0.0f;
-    return v;
+struct RbCtx {
+    int64_t M, N, K;
+    const float *A;
+    int64_t lda;
+    const float *B;
+    int64_t ldb;
+    int64_t m0, n0;   // the tile's corner (placed by tile_origin)
+    int t;
+};
+
+// Loads slice k0 .. k0+BK of the A and B tiles into registers, in MODE.
+template <class T, int MODE>
+__device__ __forceinline__ void rb_fetch(const RbCtx &c, int64_t k0, float4 (&ra)[T::AF4],
+                                         float4 (&rb)[T::BF4]) {
+    constexpr int BK = T::BK, BN = T::BN;
+#pragma unroll
+    for (int r = 0; r < T::AF4; ++r) {
+        const int f = c.t + T::THREADS * r;
+        const int m = f / (BK / 4), kq = f % (BK / 4);
+        const float *p = c.A + (c.m0 + m) * c.lda + k0 + 4 * kq;
+        if (MODE == kVec || MODE == kVecA) ra[r] = *reinterpret_cast<const float4 *>(p);
+        else if (MODE == kScalar) ra[r] = load4_scalar(p);
+        else ra[r] = load4_clamped(c.A, c.lda, c.m0 + m, k0 + 4 * kq, c.M, c.K);
+    }
+#pragma unroll
+    for (int r = 0; r < T::BF4; ++r) {
+        const int f = c.t + T::THREADS * r;
+        const int k = f / (BN / 4), nq = f % (BN / 4);
+        const float *p = c.B + (k0 + k) * c.ldb + c.n0 + 4 * nq;
+        if (MODE == kVec) rb[r] = *reinterpret_cast<const float4 *>(p);
+        else if (MODE == kVecA || MODE == kScalar) rb[r] = load4_scalar(p);
+        else rb[r] = load4_clamped(c.B, c.ldb, k0 + k, c.n0 + 4 * nq, c.K, c.N);
+    }
+}
+
+template <class T>
+__device__ __forceinline__ void rb_stage(float *as, float *bs, int t, const float4 (&ra)[T::AF4],
+                                         const float4 (&rb)[T::BF4]) {
+    constexpr int BK = T::BK, BN = T::BN;
+#pragma unroll
+    for (int r = 0; r < T::AF4; ++r) {
+        const int f = t + T::THREADS * r;
+        const int m = f / (BK / 4), kq = f % (BK / 4);
+        *reinterpret_cast<float4 *>(&as[m * T::AST + 4 * kq]) = ra[r];
+    }
+#pragma unroll
+    for (int r = 0; r < T::BF4; ++r) {
+        const int f = t + T::THREADS * r;
+        const int k = f / (BN / 4), nq = f % (BN / 4);
+        *reinterpret_cast<float4 *>(&bs[k * T::BST + 4 * nq]) = rb[r];
+    }
+}
+
+// acc += the slice held in LDS (as, bs): each LDS read of 4 k of A feeds
+// TN FMAs per k, each read of 4 columns of B feeds TM.
+template <class T>
+__device__ __forceinline__ void rb_compute(const float *as, const float *bs, int tx, int ty,
+                                           float (&acc)[T::TM][T::TN]) {
+    constexpr int BK = T::BK, TM = T::TM, TN = T::TN;
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 4) {
+        float4 a4[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            a4[i] = *reinterpret_cast<const float4 *>(&as[(ty + 16 * i) * T::AST + kk]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float b[TN];
+#pragma unroll
+            for (int g = 0; g < TN / 4; ++g) {
+                const float4 v =
+                    *reinterpret_cast<const float4 *>(&bs[(kk + q) * T::BST + 64 * g + 4 * tx]);
+                b[4 * g + 0] = v.x;
+                b[4 * g + 1] = v.y;
+                b[4 * g + 2] = v.z;
+                b[4 * g + 3] = v.w;
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const float a = q == 0 ? a4[i].x : q == 1 ? a4[i].y : q == 2 ? a4[i].z : a4[i].w;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = fmaf(a, b[j], acc[i][j]);
+            }
+        }
+        // The 8 x 8 micro-tile is issued one group of 4 k at a time (4096^3:
+        // 2651 -> 1573 us against leaving the order to the compiler); the
+        // 4 x 4 one runs better without the fence (1024^3: 53.5 against
+        // 55.6 us).
+        if constexpr (TM * TN >= 64) __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The K loop of one tile.  Slices that lie wholly inside K load in MODE
+// with no checks and no branch in the loop; the slice that runs past K (if
+// any) loads with checks.
+template <class T, int MODE>
+__device__ __forceinline__ void rb_k_loop(const RbCtx &c, float *As, float *Bs, int tx, int ty,
+                                          float (&acc)[T::TM][T::TN]) {
+    constexpr int BK = T::BK;
+    constexpr int AW = T::BM * T::AST, BW = BK * T::BST;   // words per LDS buffer
+    const int64_t slices = ceil_div(c.K, BK), full = c.K / BK;
+    if (slices == 0) return;
+    float4 ra[T::AF4], rb[T::BF4];
+    if (full > 0) rb_fetch<T, MODE>(c, 0, ra, rb);
+    else rb_fetch<T, kChecked>(c, 0, ra, rb);
+    rb_stage<T>(As, Bs, c.t, ra, rb);
+    __syncthreads();
+    int64_t s = 0;
+    for (; s + 1 < full; ++s) {
+        const int cur = static_cast<int>(s & 1);
+        rb_fetch<T, MODE>(c, (s + 1) * BK, ra, rb);
+        rb_compute<T>(As + cur * AW, Bs + cur * BW, tx, ty, acc);
+        rb_stage<T>(As + (cur ^ 1) * AW, Bs + (cur ^ 1) * BW, c.t, ra, rb);
+        __syncthreads();
+    }
+    // One or two slices are left: slice s, and the slice past K if there
+    // is one.  (Written out rather than as a loop: as a loop it made the
+    // compiler keep two slices' worth of values live and spill the 8 x 8
+    // tile's registers.)
+    if (s + 1 < slices) {
+        const int cur = static_cast<int>(s & 1);
+        rb_fetch<T, kChecked>(c, (s + 1) * BK, ra, rb);
+        rb_compute<T>(As + cur * AW, Bs + cur * BW, tx, ty, acc);
+        rb_stage<T>(As + (cur ^ 1) * AW, Bs + (cur ^ 1) * BW, c.t, ra, rb);
+        __syncthreads();
+        ++s;
+    }
+    const int cur = static_cast<int>(s & 1);
+    rb_compute<T>(As + cur * AW, Bs + cur * BW, tx, ty, acc);
 }
 
 template <class T>
@@ -73,49 +196,17 @@ void gemm_regblock_f32(int64_t M, int64_t N, int64_t K,
                        int64_t tiles_m, int64_t tiles_n,
                        int vec_a, int vec_b, int vec_c)
 {
-    constexpr int BM = T::BM, BN = T::BN, BK = T::BK, TM = T::TM, TN = T::TN;
-    constexpr int AST = T::AST, BST = T::BST;
-    __shared__ __attribute__((aligned(16))) float As[2][BM * AST];
-    __shared__ __attribute__((aligned(16))) float Bs[2][BK * BST];
+    constexpr int BM = T::BM, BN = T::BN, TM = T::TM, TN = T::TN;
+    __shared__ __attribute__((aligned(16))) float As[2 * BM * T::AST];
+    __shared__ __attribute__((aligned(16))) float Bs[2 * T::BK * T::BST];
 
     const int t = threadIdx.x;
     const int tx = t % 16, ty = t / 16;
 
     int64_t tm, tn;
     grouped_tile(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, 8, tm, tn);
-    const int64_t m0 = tm * BM, n0 = tn * BN;
-
-    float4 ra[T::AF4], rb[T::BF4];
-    auto fetch = [&](int64_t k0) {
-#pragma unroll
-        for (int r = 0; r < T::AF4; ++r) {
-            const int f = t + T::THREADS * r;
-            const int m = f / (BK / 4), kq = f % (BK / 4);
-            const int64_t gm = m0 + m, gk = k0 + 4 * kq;
-            ra[r] = load4(A + gm * lda + gk, gm < M, gk, K, vec_a);
-        }
-#pragma unroll
-        for (int r = 0; r < T::BF4; ++r) {
-            const int f = t + T::THREADS * r;
-            const int k = f / (BN / 4), nq = f % (BN / 4);
-            const int64_t gk = k0 + k, gn = n0 + 4 * nq;
-            rb[r] = load4(B + gk * ldb + gn, gk < K, gn, N, vec_b);
-        }
-    };
-    auto stage = [&](int buf) {
-#pragma unroll
-        for (int r = 0; r < T::AF4; ++r) {
-            const int f = t + T::THREADS * r;
-            const int m = f / (BK / 4), kq = f % (BK / 4);
-            *reinterpret_cast<float4 *>(&As[buf][m * AST + 4 * kq]) = ra[r];
-        }
-#pragma unroll
-        for (int r = 0; r < T::BF4; ++r) {
-            const int f = t + T::THREADS * r;
-            const int k = f / (BN / 4), nq = f % (BN / 4);
-            *reinterpret_cast<float4 *>(&Bs[buf][k * BST + 4 * nq]) = rb[r];
-        }
-    };
+    const Origin o = tile_origin<BM, BN>(tm, tn, M, N);
+    const RbCtx c{M, N, K, A, lda, B, ldb, o.m0, o.n0, t};
 
     float acc[TM][TN];
 #pragma unroll
@@ -123,77 +214,57 @@ void gemm_regblock_f32(int64_t M, int64_t N, int64_t K,
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = 0.0f;
 
-    const int64_t slices = ceil_div(K, BK);
-    if (slices > 0) {
-        fetch(0);
-        stage(0);
-        __syncthreads();
-    }
-    for (int64_t s = 0; s < slices; ++s) {
-        const int cur = static_cast<int>(s & 1);
-        if (s + 1 < slices) fetch((s + 1) * BK);
-        const float *as = As[cur];
-        const float *bs = Bs[cur];
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 4) {
-            float4 a4[TM];
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                a4[i] = *reinterpret_cast<const float4 *>(&as[(ty + 16 * i) * AST + kk]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float b[TN];
-#pragma unroll
-                for (int g = 0; g < TN / 4; ++g) {
-                    const float4 v =
-                        *reinterpret_cast<const float4 *>(&bs[(kk + q) * BST + 64 * g + 4 * tx]);
-                    b[4 * g + 0] = v.x;
-                    b[4 * g + 1] = v.y;
-                    b[4 * g + 2] = v.z;
-                    b[4 * g + 3] = v.w;
-                }
-#pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    const float a = q == 0 ? a4[i].x : q == 1 ? a4[i].y : q == 2 ? a4[i].z : a4[i].w;
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) acc[i][j] = fmaf(a, b[j], acc[i][j]);
-                }
-            }
-        }
-        if (s + 1 < slices) stage(cur ^ 1);
-        __syncthreads();
-    }
+    const bool inside = o.m0 + BM <= M && o.n0 + BN <= N;
+    if (!inside) rb_k_loop<T, kChecked>(c, As, Bs, tx, ty, acc);
+    else if (vec_a && vec_b && (o.n0 & 3) == 0) rb_k_loop<T, kVec>(c, As, Bs, tx, ty, acc);
+    else if (vec_a) rb_k_loop<T, kVecA>(c, As, Bs, tx, ty, acc);
+    else rb_k_loop<T, kScalar>(c, As, Bs, tx, ty, acc);
 
-    // Epilogue: masked stores, float4 when the row segment is whole and aligned.
+    // Epilogue: rows and columns of the tile that it owns (a moved tile's
+    // first skip_m rows and skip_n columns belong to the tile before it),
+    // float4 stores where four columns are owned, in range and aligned.
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-        const int64_t gm = m0 + ty + 16 * i;
-        if (gm >= M) continue;
+        const int r = ty + 16 * i;
+        const int64_t gm = o.m0 + r;
+        if (r < o.skip_m || gm >= M) continue;
         float *crow = C + gm * ldc;
 #pragma unroll
         for (int g = 0; g < TN / 4; ++g) {
-            const int64_t gn = n0 + 64 * g + 4 * tx;
+            const int col = 64 * g + 4 * tx;
+            const int64_t gn = o.n0 + col;
             const float *v = &acc[i][4 * g];
-            if (vec_c && gn + 3 < N) {
+            if (vec_c && col >= o.skip_n && gn + 3 < N && (gn & 3) == 0) {
                 *reinterpret_cast<float4 *>(crow + gn) = make_float4(v[0], v[1], v[2], v[3]);
             } else {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    if (gn + j < N) crow[gn + j] = v[j];
+                    if (col + j >= o.skip_n && gn + j < N) crow[gn + j] = v[j];
             }
         }
     }
 }
 
-// 128 x 128 tiles with 8 x 8 micro-tiles; 64 x 64 tiles with 4 x 4 when the
-// large tiles would leave CUs idle (fewer than one per CU: 1024^3 has 64).
+// 128 x 128 tiles with 8 x 8 micro-tiles, or 64 x 64 tiles with 4 x 4.
+// The large tile runs best at two or more tiles per CU (three workgroups
+// fit on one); it is used when there are at least 2 x 256 of them and they
+// split over the CUs about as evenly as the small ones.  Measured on
+// MI355X: 2048^3 (256 large tiles) 342 -> 230 us on small tiles; 3072^3
+// (576 large tiles, 2.25 a CU) 877 -> 731 us; 2048x4096x2048 (512) and
+// 4096^3 (1024) faster on large ones (394 against 435 us).
 using RegLarge = RegTile<128, 128, 8, 8>;
 using RegSmall = RegTile<64, 64, 4, 4>;
 
 constexpr int64_t kCUs = 256;
 
 bool small_tiles(int64_t M, int64_t N) {
-    return ceil_div(M, RegLarge::BM) * ceil_div(N, RegLarge::BN) < kCUs;
+    const int64_t large = ceil_div(M, RegLarge::BM) * ceil_div(N, RegLarge::BN);
+    const int64_t small = ceil_div(M, RegSmall::BM) * ceil_div(N, RegSmall::BN);
+    if (large < 2 * kCUs) return true;
+    // rounds of tiles per CU over the ideal, for each size
+    const double waste_large = static_cast<double>(ceil_div(large, kCUs) * kCUs) / large;
+    const double waste_small = static_cast<double>(ceil_div(small, kCUs) * kCUs) / small;
+    return waste_large > 1.1 * waste_small;
 }
 
 template <class T>
