@@ -228,3 +228,20 @@ def test_caller_workspace_checked_on_host():
 def test_auto_choice(shape, rung):
     d = tra.tra_gemm_describe(tra.AUTO, *shape)
     assert f"rung={rung} " in d, d
+
+
+@pytest.mark.parametrize("shape,tile", [
+    ((1024, 1024, 1024), "<64x64x16, 4 waves>"),            # K <= 1024
+    ((3000, 2049, 1531), "<64x64x16, 4 waves, 4 sets>"),    # 128x128 would waste the edge
+    ((4096, 4096, 4096), "<256x128x16, 8 waves, 4 sets>"),  # 4 tiles of 128x128 a CU
+    ((4096, 2048, 1024), "<256x128x16, 8 waves, 4 sets>"),  # exactly 256 tiles of 256x128
+    ((2048, 4096, 2048), "<256x128x16, 8 waves, 4 sets>"),
+    ((2048, 2048, 2048), "<128x128x16, 8 waves>"),          # one 128x128 tile a CU
+    ((2304, 2304, 2304), "<128x128x16, 8 waves>"),          # 324 tiles, long K
+    ((2000, 2600, 3000), "<128x128x16, 8 waves>"),          # 336 tiles, edges wasted no worse
+    ((3000, 3000, 1000), "<64x64x16, 4 waves>"),            # short K stays on 64x64
+    ((3072, 3072, 3072), "<64x64x16, 4 waves, 4 sets>"),    # 576 tiles: 2.25 a CU
+])
+def test_auto_tile_class(shape, tile):
+    d = tra.tra_gemm_describe(tra.AUTO, *shape)
+    assert f"kernel=gemm_mfma_f32{tile} " in d, d

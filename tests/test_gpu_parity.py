@@ -251,6 +251,8 @@ MFMA_TILE_SHAPES = [
     (200, 300, 4100, "<64x64x16, 4 waves, 4 sets>"),   # few tiles, long K
     (300, 500, 203, "<64x64x16, 4 waves>"),       # few tiles
     (700, 900, 1500, "<64x64x16, 4 waves, 4 sets>"),   # 165 tiles, K > 1024
+    (2040, 4090, 300, "<256x128x16, 8 waves, 4 sets>"),   # 8 x 32 = 256 tiles of 256 x 128
+    (2000, 2600, 2050, "<128x128x16, 8 waves>"),  # 336 tiles of 128 x 128, K >= 2048
 ]
 
 

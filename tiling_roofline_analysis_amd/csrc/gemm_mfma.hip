@@ -591,9 +591,10 @@ void gemm_mfma_f32_sk(int64_t M, int64_t N, int64_t K,
 // Tile shapes (chosen by timing candidates on MI355X, interleaved and
 // repeated on one warm GPU):
 //   Large  256x128x16, 8 waves of 64x64, four register sets: shapes with
-//          at least 4 tiles of 128x128 per CU (4096^3: 512 such tiles).
+//          at least 4 tiles of 128x128 per CU (4096^3: 512 such tiles), or
+//          a whole number of 256x128 tiles per CU.
 //   Mid    128x128x16, 8 waves of 64x32: about one 128x128 tile per CU
-//          (2048^3: 256 tiles).
+//          (2048^3: 256 tiles), or one to two per CU with K >= 2048.
 //   Many   64x64x16, 4 waves of 32x32, two register sets: every other
 //          shape with K <= 1024 (1024^3).
 //   Deep   the Many tile with four register sets in flight, for K > 1024
@@ -610,10 +611,27 @@ constexpr int64_t kMi355xCUs = 256;
 
 enum class Shape { kLarge, kMid, kMany, kDeep };
 
+// Fraction of a padded bm x bn tile grid that lies inside M x N.
+double cover(int64_t M, int64_t N, int64_t bm, int64_t bn) {
+    return static_cast<double>(M) * static_cast<double>(N) /
+           (static_cast<double>(ceil_div(M, bm) * bm) * static_cast<double>(ceil_div(N, bn) * bn));
+}
+
 Shape pick(int64_t M, int64_t N, int64_t K) {
+    const int64_t cus = kMi355xCUs;
     const int64_t tiles128 = ceil_div(M, 128) * ceil_div(N, 128);
-    if (tiles128 >= 4 * kMi355xCUs) return Shape::kLarge;
-    if (4 * tiles128 > 3 * kMi355xCUs && tiles128 <= kMi355xCUs) return Shape::kMid;
+    const int64_t large = ceil_div(M, 256) * ceil_div(N, 128);
+    // Large: about 4 tiles of 128x128 per CU, or a whole number of 256x128
+    // tiles per CU (4096x2048x1024: 135 -> 126 us against 64x64 tiles)
+    if (tiles128 >= 4 * cus || (large >= cus && large % cus == 0)) return Shape::kLarge;
+    if (4 * tiles128 > 3 * cus && tiles128 <= cus) return Shape::kMid;
+    // Mid also for one to two 128x128 tiles per CU once K is long enough to
+    // pay for the stream-K split that evens them out, unless 128x128 tiles
+    // waste more of the edges (3000x2049x1531 stays on 64x64 tiles):
+    // 2304^3 207 -> 193 us, 1536x4096x4096 386 -> 382 us
+    if (tiles128 > cus && tiles128 < 2 * cus && K >= 2048 &&
+        cover(M, N, 128, 128) >= 0.97 * cover(M, N, 64, 64))
+        return Shape::kMid;
     return K > 1024 ? Shape::kDeep : Shape::kMany;
 }
 
