@@ -210,7 +210,7 @@ def test_caller_workspace_checked_on_host():
     ((1024, 1024, 1024), "mfma"),          # 256 tiles on 256 CUs
     ((4096, 4096, 4096), "mfma"),          # 1024 tiles, 4 a CU
     ((3000, 2049, 1531), "mfma_streamk"),  # 1551 tiles: 6.06 a CU
-    ((4608, 4608, 4096), "mfma_streamk"),  # 1296 tiles: 5.06 a CU
+    ((4608, 4608, 4096), "mfma_streamk"),  # 648 tiles of 256 x 128: 2.53 a CU
     ((3072, 3072, 3072), "mfma"),          # 2304 tiles: 9 a CU
     ((3008, 2048, 1536), "mfma"),          # 1504 tiles: 5.875 a CU, 2% short
     ((1500, 1500, 77), "mfma"),            # 3 slices of K: nothing to share
@@ -220,6 +220,8 @@ def test_caller_workspace_checked_on_host():
     ((300, 500, 203), "mfma"),             # 40 tiles of 7 slices: too short to share
     ((100, 100, 300), "mfma"),             # 4 tiles of 10 slices: saves < 8 us
     ((100, 100, 2000), "mfma_streamk"),    # 4 tiles of 63 slices
+    ((3000, 3000, 1000), "mfma_streamk"),  # 2209 tiles: 8.63 a CU, 4.3% uneven
+    ((3500, 3500, 1500), "mfma"),          # 3025 tiles: 11.82 a CU, 1.6% uneven
     ((8192, 64, 2048), "mfma_streamk"),    # 128 tiles: exactly half the CUs
     ((4096, 128, 2048), "mfma_streamk"),   # 128 tiles
     ((12288, 64, 2048), "mfma"),           # 192 tiles, 2 GFLOP: too small to split

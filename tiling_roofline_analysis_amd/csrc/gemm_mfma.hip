@@ -779,10 +779,12 @@ LaunchPlan plan_mfma(int64_t M, int64_t N, int64_t K, bool stream_k) {
 //     second launch (8 us; 200x300x4100: 20 tiles, 67 -> ~20 us; exactly
 //     half, 8192x64x2048: 128 tiles, 37 -> 29 us);
 //   * otherwise when one tile per workgroup would leave some CUs a whole
-//     tile more work than the mean (at least 10% more: e.g. 1296 tiles on
-//     256 CUs, 5.06 a CU, so some CUs run 6) and the product is large
-//     enough (>= 4 GFLOP) to hide the second launch.  Shapes that split
-//     evenly over the CUs, like 2304 tiles on 256, stay data-parallel.
+//     tile more work than the mean (at least 4% more: e.g. 2209 tiles on
+//     256 CUs, 8.63 a CU, so some CUs run 9; 3000x3000x1000 165 -> 159 us)
+//     and the product is large enough (>= 4 GFLOP) to hide the second
+//     launch.  Shapes that split evenly over the CUs, like 2304 tiles on
+//     256, stay data-parallel; below 4% the split did not pay (3500x3500x
+//     1500, 1.6%: 313 against 318 us).
 template <class T>
 bool stream_k_pays(int64_t M, int64_t N, int64_t K) {
     const SkPlan p = plan_split<T>(M, N, K, true);
@@ -798,7 +800,7 @@ bool stream_k_pays(int64_t M, int64_t N, int64_t K) {
     if (2.0 * static_cast<double>(M) * static_cast<double>(N) * static_cast<double>(K) < 4e9)
         return false;
     const int64_t per_cu = ceil_div(tiles, cus);
-    return static_cast<double>(per_cu * cus) >= 1.1 * static_cast<double>(tiles);
+    return static_cast<double>(per_cu * cus) >= 1.04 * static_cast<double>(tiles);
 }
 
 bool prefer_stream_k(int64_t M, int64_t N, int64_t K) {
