@@ -33,13 +33,21 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
-def test_only_abi_symbols_are_exported():
+@pytest.mark.parametrize("path", [tra.LIB_PATH, tra.POISON_LIB_PATH], ids=["product", "poison"])
+def test_only_abi_symbols_are_exported(path):
     import subprocess
-    out = subprocess.run(["nm", "-D", "--defined-only", tra.LIB_PATH], capture_output=True,
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True,
                          text=True, check=True).stdout
     syms = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     ours = {s for s in syms if not s.startswith("_")}
     assert ours == set(tra.ABI_FUNCTIONS), ours
+
+
+def test_poison_library_loads_with_every_declared_symbol():
+    plib = tra.load_poisoned()
+    for name in header_functions():
+        assert hasattr(plib, name), name
+    assert plib is not tra.load()
 
 
 def test_status_and_variant_names():

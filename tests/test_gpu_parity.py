@@ -336,10 +336,14 @@ def test_rungs_agree_bitwise_on_int_patterns_1024():
 
 @pytest.mark.parametrize("name", ["uniform1024", "ragged"])
 def test_mfma_deterministic(name):
+    # bitwise the same over 10 runs, for each MFMA form (the stream-K partial
+    # sums are added in a fixed K order, not in the order workgroups finish)
     A, B = workload_inputs(name)
-    first = run_gpu(tra.MFMA, A, B)[0]
-    for _ in range(3):
-        assert np.array_equal(run_gpu(tra.MFMA, A, B)[0].view(np.uint32), first.view(np.uint32))
+    for variant in (tra.MFMA, tra.MFMA_STREAMK, tra.AUTO):
+        first = run_gpu(variant, A, B)[0]
+        for _ in range(9):
+            again = run_gpu(variant, A, B)[0]
+            assert np.array_equal(again.view(np.uint32), first.view(np.uint32)), variant
 
 
 def test_auto_is_mfma():

@@ -23,6 +23,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtra_gemm.so")
+POISON_LIB_PATH = os.path.join(HERE, "libtra_gemm_poison.so")
 
 # tra_status
 TRA_OK = 0
@@ -71,10 +72,31 @@ def load() -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
+    _lib = _open(LIB_PATH)
+    return _lib
+
+
+def load_poisoned() -> ctypes.CDLL:
+    """The test build of the library (libtra_gemm_poison.so): the same
+    entry points, with every kernel filling its LDS with NaN before use.
+    For tests only; a separate handle from load()."""
+    return _open(POISON_LIB_PATH)
+
+
+def _open(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
         raise RuntimeError(
-            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
-    lib = ctypes.CDLL(LIB_PATH)
+            f"{path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    # PyTorch ships its own libamdhip64.so.7, with the same soname as ROCm's.
+    # Whichever is loaded first is the one HIP runtime of the process, and
+    # the library's launches failed when it brought in ROCm's copy ahead of
+    # torch's.  So torch, which owns the device buffers and streams passed
+    # in, is loaded first when it is installed.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(path)
     i64, p, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     lib.gemm_f32.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
     lib.gemm_f32.restype = c_int
@@ -102,7 +124,6 @@ def load() -> ctypes.CDLL:
     lib.tra_probe_mfma_f32.restype = c_int
     lib.tra_probe_fma_f32.argtypes = [i64, p, p]
     lib.tra_probe_fma_f32.restype = c_int
-    _lib = lib
     return lib
 
 

@@ -90,6 +90,27 @@ __device__ __forceinline__ void grouped_tile(int64_t id, int64_t tiles_m, int64_
     tn = in / rows;
 }
 
+// ---- LDS poison (test builds) ----
+//
+// Built with TRA_LDS_POISON=1 (libtra_gemm_poison.so, for the tests), every
+// kernel that stages operands in LDS first fills its LDS with a quiet NaN,
+// so that a read of any word that no lane staged -- a wrong index, a row
+// padding word, a slice read before it was stored -- makes C NaN, which the
+// exact parity checks catch.  In the product build this is nothing.
+#ifndef TRA_LDS_POISON
+#define TRA_LDS_POISON 0
+#endif
+
+__device__ __forceinline__ void lds_poison(float *lds, int words) {
+    if constexpr (TRA_LDS_POISON != 0) {
+        const int nt = static_cast<int>(blockDim.x * blockDim.y * blockDim.z);
+        const int t = static_cast<int>(threadIdx.x +
+                                       blockDim.x * (threadIdx.y + blockDim.y * threadIdx.z));
+        for (int i = t; i < words; i += nt) lds[i] = __int_as_float(0x7fc00000);
+        __syncthreads();
+    }
+}
+
 // ---- operand loads and tile placement shared by the tiled rungs ----
 
 // X[row][col .. col+3] of a rows x cols row-major matrix, zero outside it.

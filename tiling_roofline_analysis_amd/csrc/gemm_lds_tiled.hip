@@ -37,6 +37,8 @@ void gemm_lds_tiled_f32(int64_t M, int64_t N, int64_t K,
 {
     __shared__ float As[kTile][kTile];
     __shared__ float Bs[kTile][kTile];
+    lds_poison(&As[0][0], kTile * kTile);
+    lds_poison(&Bs[0][0], kTile * kTile);
 
     const int tx = threadIdx.x, ty = threadIdx.y;
     const int64_t bid = blockIdx.x;

@@ -512,6 +512,7 @@ void gemm_mfma_f32(int64_t M, int64_t N, int64_t K,
                    int vec_c)
 {
     __shared__ __attribute__((aligned(16))) float lds[T::LDS_WORDS];
+    lds_poison(lds, T::LDS_WORDS);
 
     const int bid = static_cast<int>(blockIdx.x);
     const int fix = p.sk_tiles * fix_chunks<T>();
@@ -543,6 +544,7 @@ void gemm_mfma_f32_sk(int64_t M, int64_t N, int64_t K,
                       float *__restrict__ C, int64_t ldc, SkPlan p, int vec_a, int vec_b)
 {
     __shared__ __attribute__((aligned(16))) float lds[T::LDS_WORDS];
+    lds_poison(lds, T::LDS_WORDS);
 
     const int ipt = static_cast<int>(p.ipt);
     const int w = static_cast<int>(xcd_remap(blockIdx.x, p.sk_wgs));

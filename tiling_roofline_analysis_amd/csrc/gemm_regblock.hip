@@ -199,6 +199,8 @@ void gemm_regblock_f32(int64_t M, int64_t N, int64_t K,
     constexpr int BM = T::BM, BN = T::BN, TM = T::TM, TN = T::TN;
     __shared__ __attribute__((aligned(16))) float As[2 * BM * T::AST];
     __shared__ __attribute__((aligned(16))) float Bs[2 * T::BK * T::BST];
+    lds_poison(As, 2 * BM * T::AST);
+    lds_poison(Bs, 2 * T::BK * T::BST);
 
     const int t = threadIdx.x;
     const int tx = t % 16, ty = t / 16;
