@@ -34,6 +34,8 @@ SHAPES = [
     (2040, 4090, 300),    # 256 tiles of 256 x 128
     (2000, 2600, 2050),   # 128 x 128 with stream-K
     (3000, 2049, 1531),   # the ragged configuration
+    (3000, 32, 1100),     # narrower than a tile: float4 loads, column quads past N zeroed
+    (40, 2000, 700),      # shorter than a tile: float4 loads, rows past M zeroed
 ]
 
 

@@ -253,6 +253,8 @@ MFMA_TILE_SHAPES = [
     (700, 900, 1500, "<64x64x16, 4 waves, 4 sets>"),   # 165 tiles, K > 1024
     (2040, 4090, 300, "<256x128x16, 8 waves, 4 sets>"),   # 8 x 32 = 256 tiles of 256 x 128
     (2000, 2600, 2050, "<128x128x16, 8 waves>"),  # 336 tiles of 128 x 128, K >= 2048
+    (3000, 32, 1100, "<64x64x16, 4 waves, 4 sets>"),   # narrower than a tile (float4 loads)
+    (40, 2000, 700, "<64x64x16, 4 waves>"),       # shorter than a tile (float4 loads)
 ]
 
 
@@ -282,7 +284,8 @@ def stride_case(M, N, K):
 
 
 @pytest.mark.parametrize("layout", ["padded_aligned", "padded_misaligned"])
-@pytest.mark.parametrize("shape", [(300, 200, 150), (4000, 4200, 203), (1500, 1500, 77)],
+@pytest.mark.parametrize("shape", [(300, 200, 150), (4000, 4200, 203), (1500, 1500, 77),
+                                   (50, 36, 300)],
                          ids=lambda s: f"{s[0]}x{s[1]}x{s[2]}")
 @pytest.mark.parametrize("variant", RUNGS, ids=RUNG_IDS)
 def test_strides_and_alignment(variant, shape, layout):

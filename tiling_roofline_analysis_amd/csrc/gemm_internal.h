@@ -117,7 +117,9 @@ __device__ __forceinline__ void lds_poison(float *lds, int words) {
 // Addresses are clamped into the matrix, so every load is valid, and the
 // zero is applied with an AND mask on the loaded bits: the loads are
 // unconditional (a select would let the compiler predicate each load behind
-// a branch and wait for it).
+// a branch and wait for it).  The mask does make the wave wait for the load
+// (and every load before it) where it is applied, which is cheap for the
+// one slice per tile that runs past K but not for a whole K loop.
 __device__ __forceinline__ float4 load4_clamped(const float *X, int64_t ld, int64_t row,
                                                 int64_t col, int64_t rows, int64_t cols) {
     const bool rok = row < rows;
@@ -133,6 +135,19 @@ __device__ __forceinline__ float4 load4_clamped(const float *X, int64_t ld, int6
     return make_float4(v[0], v[1], v[2], v[3]);
 }
 
+// Sixteen zero bytes in device memory (one copy per code object), read in
+// place of a float4 that lies outside a matrix.
+static __device__ __attribute__((aligned(16))) float g_zero4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+
+// X[row][col .. col+3] as one float4 where that quad lies inside the matrix
+// (`in`), else +0: for 16-byte aligned rows and a quad that is wholly
+// inside or wholly outside.  The choice is an address select made before
+// the load, so nothing waits for the loaded value until it is used.
+__device__ __forceinline__ float4 load4_quad(const float *X, int64_t ld, int64_t row,
+                                             int64_t col, bool in) {
+    return *reinterpret_cast<const float4 *>(in ? X + row * ld + col : &g_zero4[0]);
+}
+
 // How a slice is loaded from global memory.  A tile is always placed
 // inside the matrices when they are at least one tile large (see
 // tile_origin below), so only the slice that runs past K and matrices
@@ -141,9 +156,12 @@ __device__ __forceinline__ float4 load4_clamped(const float *X, int64_t ld, int6
 //   kVecA     A aligned, B not (ldb or the tile's first column not a
 //             multiple of 4): float4 loads of A, element loads of B;
 //   kScalar   element loads of both;
-//   kChecked  element loads at clamped addresses with zeros outside the
-//             matrices (the k tail slice, and tiles larger than the matrix).
-enum LoadMode { kVec = 0, kVecA = 1, kScalar = 2, kChecked = 3 };
+//   kChecked  element loads with zeros outside the matrices (the k tail
+//             slice, and tiles larger than the matrix);
+//   kEdge     full slices of a tile larger than the matrix when A and B are
+//             aligned and N is a multiple of 4: float4 loads, zeros past
+//             row M of A and column N of B.
+enum LoadMode { kVec = 0, kVecA = 1, kScalar = 2, kChecked = 3, kEdge = 4 };
 
 __device__ __forceinline__ float4 load4_scalar(const float *p) {
     return make_float4(p[0], p[1], p[2], p[3]);
