@@ -36,6 +36,7 @@ SHAPES = [
     (3000, 2049, 1531),   # the ragged configuration
     (3000, 32, 1100),     # narrower than a tile: float4 loads, column quads past N zeroed
     (40, 2000, 700),      # shorter than a tile: float4 loads, rows past M zeroed
+    (3000, 33, 1100),     # narrower than a tile, N odd: element loads
 ]
 
 

@@ -255,6 +255,7 @@ MFMA_TILE_SHAPES = [
     (2000, 2600, 2050, "<128x128x16, 8 waves>"),  # 336 tiles of 128 x 128, K >= 2048
     (3000, 32, 1100, "<64x64x16, 4 waves, 4 sets>"),   # narrower than a tile (float4 loads)
     (40, 2000, 700, "<64x64x16, 4 waves>"),       # shorter than a tile (float4 loads)
+    (3000, 33, 1100, "<64x64x16, 4 waves, 4 sets>"),   # narrower than a tile, N odd
 ]
 
 

@@ -148,6 +148,18 @@ __device__ __forceinline__ float4 load4_quad(const float *X, int64_t ld, int64_t
     return *reinterpret_cast<const float4 *>(in ? X + row * ld + col : &g_zero4[0]);
 }
 
+// X[row][col .. col+3] element by element, for a row that lies inside the
+// matrix when `row_in`, with +0 for row_in false and for columns at or past
+// `cols`; each element outside reads the zero word, as in load4_quad.
+__device__ __forceinline__ float4 load4_elems(const float *X, int64_t ld, int64_t row,
+                                              int64_t col, bool row_in, int64_t cols) {
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        v[e] = *(row_in && col + e < cols ? X + row * ld + col + e : &g_zero4[0]);
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+
 // How a slice is loaded from global memory.  A tile is always placed
 // inside the matrices when they are at least one tile large (see
 // tile_origin below), so only the slice that runs past K and matrices
@@ -160,8 +172,10 @@ __device__ __forceinline__ float4 load4_quad(const float *X, int64_t ld, int64_t
 //             slice, and tiles larger than the matrix);
 //   kEdge     full slices of a tile larger than the matrix when A and B are
 //             aligned and N is a multiple of 4: float4 loads, zeros past
-//             row M of A and column N of B.
-enum LoadMode { kVec = 0, kVecA = 1, kScalar = 2, kChecked = 3, kEdge = 4 };
+//             row M of A and column N of B;
+//   kEdgeElem full slices of a tile larger than the matrix otherwise:
+//             element loads, zeros past row M of A and column N of B.
+enum LoadMode { kVec = 0, kVecA = 1, kScalar = 2, kChecked = 3, kEdge = 4, kEdgeElem = 5 };
 
 __device__ __forceinline__ float4 load4_scalar(const float *p) {
     return make_float4(p[0], p[1], p[2], p[3]);

@@ -51,8 +51,9 @@
 // when the rows are aligned and N is a multiple of 4: a quad outside the
 // matrix reads a zero word instead, chosen by address, so no mask has to
 // wait for the load (masking every slice where it is loaded made each
-// slice wait out the memory latency: 16384x32x16384 took 1114 us, now
-// 319 us).  Otherwise they load like the slice past K.
+// slice wait out the memory latency: 16384x32x16384 took 1109 us, now
+// 327 us).  Otherwise they load single elements, each element outside the
+// matrices from the zero word.
 //
 // Workgroup ids are remapped so each of the 8 XCDs runs a compact patch of
 // tiles (shared L2 traffic), in groups of 8 tile rows.
@@ -121,6 +122,8 @@ __device__ __forceinline__ void fetch(const Ctx<T> &c, int64_t k0, float4 (&ra)[
         else if (MODE == kScalar) ra[r] = load4_scalar(p);
         else if (MODE == kEdge)
             ra[r] = load4_quad(c.A, c.lda, c.m0 + m, k0 + 4 * kq, c.m0 + m < c.M);
+        else if (MODE == kEdgeElem)
+            ra[r] = load4_elems(c.A, c.lda, c.m0 + m, k0 + 4 * kq, c.m0 + m < c.M, c.K);
         else ra[r] = load4_clamped(c.A, c.lda, c.m0 + m, k0 + 4 * kq, c.M, c.K);
     }
 #pragma unroll
@@ -133,6 +136,8 @@ __device__ __forceinline__ void fetch(const Ctx<T> &c, int64_t k0, float4 (&ra)[
         else if (MODE == kVecA || MODE == kScalar) rb[r] = load4_scalar(p);
         else if (MODE == kEdge)
             rb[r] = load4_quad(c.B, c.ldb, k0 + k, c.n0 + 4 * nq, c.n0 + 4 * nq < c.N);
+        else if (MODE == kEdgeElem)
+            rb[r] = load4_elems(c.B, c.ldb, k0 + k, c.n0 + 4 * nq, true, c.N);
         else rb[r] = load4_clamped(c.B, c.ldb, k0 + k, c.n0 + 4 * nq, c.K, c.N);
     }
 }
@@ -426,7 +431,7 @@ __device__ __forceinline__ void tile_pass(const Ctx<T> &c, int vec_a, int vec_b,
         if (!inside && quads)
             k_loop<T, kEdge>(c, lds, wm0 + l32, wn0 + l32, kbase, acc, s0, n);
         else if (!inside)
-            k_loop<T, kChecked>(c, lds, wm0 + l32, wn0 + l32, kbase, acc, s0, n);
+            k_loop<T, kEdgeElem>(c, lds, wm0 + l32, wn0 + l32, kbase, acc, s0, n);
         else if (vec_a && vec_b && (c.n0 & 3) == 0)
             k_loop<T, kVec>(c, lds, wm0 + l32, wn0 + l32, kbase, acc, s0, n);
         else if (vec_a)
