@@ -25,7 +25,10 @@
  * allocates nothing; gemm_f32 and gemm_f32_variant use a workspace that the
  * library allocates on first need for each (device, stream) pair and keeps
  * until the process ends (it grows, after synchronising that stream, when a
- * later call needs more).
+ * later call needs more).  The pair is keyed by the stream's handle, and
+ * calls on one handle rely on the stream's order: synchronise a stream that
+ * has such calls in flight before destroying it, since a stream created
+ * later may be given the same handle.
  *
  * Asynchrony: gemm_f32 and gemm_f32_variant return once the kernels are
  * enqueued on `stream` (a hipStream_t; NULL means the null stream of the

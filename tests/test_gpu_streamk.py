@@ -137,3 +137,44 @@ def test_auto_uses_the_split_where_it_pays():
     C2 = tra.matmul(A, B, variant=tra.MFMA_STREAMK)
     torch.cuda.synchronize()
     assert torch.equal(C1, C2)
+
+
+def test_threads_on_their_own_streams_share_the_library_safely():
+    # four threads, each on its own stream, alternate a small and a large
+    # stream-K shape without synchronising, so the library's per-stream
+    # workspaces are created and grown while the other threads launch; every
+    # result must equal the single-threaded one bit for bit (the split's
+    # reduction order is fixed)
+    import threading
+    import torch
+    shapes = [(300, 500, 203), (4000, 4200, 203)]
+    operands, expect = {}, {}
+    for M, N, K in shapes:
+        A, B = dev(inputs.uniform(M, K, M + 1)), dev(inputs.uniform(K, N, N + 2))
+        operands[(M, N, K)] = (A, B)
+        expect[(M, N, K)] = tra.matmul(A, B, variant=tra.MFMA_STREAMK)
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    plan = {(t, i): shapes[(t + i) % 2] for t in range(4) for i in range(6)}
+    outs = {key: torch.full((s[0], s[1]), float("nan"), device="cuda:0")
+            for key, s in plan.items()}
+    torch.cuda.synchronize()
+    failures = []
+
+    def work(t):
+        for i in range(6):
+            M, N, K = plan[(t, i)]
+            A, B = operands[(M, N, K)]
+            st = tra.gemm_f32_variant(tra.MFMA_STREAMK, M, N, K, A.data_ptr(), K, B.data_ptr(),
+                                      N, outs[(t, i)].data_ptr(), N, streams[t].cuda_stream)
+            if st != tra.TRA_OK:
+                failures.append((t, i, tra.tra_status_string(st)))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not failures, failures
+    for key, C in outs.items():
+        assert torch.equal(C, expect[plan[key]]), key
