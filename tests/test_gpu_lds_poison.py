@@ -37,6 +37,7 @@ SHAPES = [
     (3000, 32, 1100),     # narrower than a tile: float4 loads, column quads past N zeroed
     (40, 2000, 700),      # shorter than a tile: float4 loads, rows past M zeroed
     (3000, 33, 1100),     # narrower than a tile, N odd: element loads
+    (200, 66000, 40),     # 256 x 128 tiles taller than M
 ]
 
 

@@ -256,6 +256,8 @@ MFMA_TILE_SHAPES = [
     (3000, 32, 1100, "<64x64x16, 4 waves, 4 sets>"),   # narrower than a tile (float4 loads)
     (40, 2000, 700, "<64x64x16, 4 waves>"),       # shorter than a tile (float4 loads)
     (3000, 33, 1100, "<64x64x16, 4 waves, 4 sets>"),   # narrower than a tile, N odd
+    (200, 66000, 40, "<256x128x16, 8 waves, 4 sets>"),   # large tiles taller than M
+    (100, 30001, 40, "<128x128x16, 8 waves>"),    # 128 x 128 tiles taller than M, N odd
 ]
 
 
