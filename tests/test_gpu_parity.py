@@ -424,3 +424,23 @@ def test_random_shapes_small_ints_exact(variant):
         assert_exact(C, ref.c32, f"{M}x{N}x{K} aligned={aligned}")
         full = buf[off:off + M * ldc_].reshape(M, ldc_)
         assert np.all(full[:, N:] == C_SENTINEL), "wrote past column N"
+
+
+@pytest.mark.parametrize("shape", [(150, 130, 70), (300, 500, 203), (40, 2000, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("variant", RUNGS + [tra.AUTO], ids=RUNG_IDS + ["auto"])
+def test_non_finite_inputs_propagate(variant, shape):
+    # IEEE propagation: an infinity or NaN in A or B reaches exactly the
+    # elements of C whose sums use it (inf * 0 = NaN, inf + -inf = NaN); the
+    # other terms are small integers, so every summation order gives the
+    # oracle's value, and the zeros a kernel pads with never meet them
+    M, N, K = shape
+    A = inputs.small_ints(M, K, 11)
+    B = inputs.small_ints(K, N, 12)
+    A[3, 5], A[M - 1, K // 2], A[M // 2, K - 1] = np.inf, -np.inf, np.nan
+    B[K // 3, 4], B[K - 1, N - 1] = np.inf, -np.inf
+    ref = oracle.gemm(A, B).c32
+    assert np.isnan(ref).any() and np.isinf(ref).any()
+    C, *_ = run_gpu(variant, A, B)
+    same = (C == ref) | (np.isnan(C) & np.isnan(ref))
+    assert same.all(), f"{int((~same).sum())} elements differ; first at {np.argwhere(~same)[0]}"
