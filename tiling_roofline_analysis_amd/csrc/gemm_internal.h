@@ -168,8 +168,9 @@ __device__ __forceinline__ float4 load4_elems(const float *X, int64_t ld, int64_
 //   kVecA     A aligned, B not (ldb or the tile's first column not a
 //             multiple of 4): float4 loads of A, element loads of B;
 //   kScalar   element loads of both;
-//   kChecked  element loads with zeros outside the matrices (the k tail
-//             slice, and tiles larger than the matrix);
+//   kChecked  element loads with zeros outside the matrices: the k tail
+//             slice, and in the register-blocked rung the tiles larger than
+//             the matrix;
 //   kEdge     full slices of a tile larger than the matrix when A and B are
 //             aligned and N is a multiple of 4: float4 loads, zeros past
 //             row M of A and column N of B;
