@@ -88,16 +88,20 @@ typedef enum tra_status {
  *                of resident workgroups (the tile-size versus occupancy
  *                trade-off of page "Roofline & Tiling notes",
  *                legato-user-group.github.io/tensor2silicon-lab/week04/
- *                researchers/jaehyeong, key points), the last partial wave
- *                plus one full wave of tiles is cut into K slices and shared
- *                out evenly over one wave of workgroups (the stream-K
- *                decomposition of Osama et al., "Stream-K: Work-centric
- *                Parallel Decomposition for Dense Matrix-Matrix
- *                Multiplication on the GPU", 2023).  Tiles split between
- *                workgroups are summed by a second kernel in K order, so
- *                results are deterministic.  Needs a device workspace of
- *                tra_gemm_workspace_size() bytes; without a split it runs
- *                the MFMA launch.
+ *                researchers/jaehyeong, key points), the tiles of the last
+ *                partial wave are split along K, in one of two forms:
+ *                "parts", when they fit in half a wave and spread evenly,
+ *                each tile cut into up to 8 equal runs of K slices that run
+ *                in the same launch as the other tiles; otherwise "runs",
+ *                their slices shared out evenly over one wave of
+ *                workgroups in a launch of their own, a run crossing tiles
+ *                (the stream-K decomposition of Osama et al., "Stream-K:
+ *                Work-centric Parallel Decomposition for Dense Matrix-
+ *                Matrix Multiplication on the GPU", 2023).  The partial
+ *                sums of each split tile are added in K order by a second
+ *                kernel, so results are deterministic.  Needs a device
+ *                workspace of tra_gemm_workspace_size() bytes; without a
+ *                split it runs the MFMA launch.
  *   AUTO         the library's choice for the shape: MFMA, or MFMA_STREAMK
  *                where a split is predicted to pay.
  */
@@ -183,10 +187,11 @@ TRA_API tra_status tra_gemm_workspace_size(int variant, int64_t M, int64_t N, in
  * tra_gemm_describe: writes a one-line, NUL-terminated description of the
  * launch that gemm_f32_variant(variant, M, N, K, ...) would make for
  * 16-byte-aligned operands with lda = K, ldb = N, ldc = N (kernel name, tile
- * shape, grid and block size, stream-K tiles and workgroups, workspace
- * bytes) into buf[0 .. len-1].  Launches nothing; the stream-K split is
- * planned for the current device's CU count, or MI355X's 256 CUs when no
- * device is present.  Returns TRA_OK, or TRA_ERR_INVALID_ARG for an
+ * shape, grid and block size, the split tiles and the workgroups that run
+ * them, the form of the split -- "parts" or "runs", see
+ * TRA_GEMM_MFMA_STREAMK -- and workspace bytes) into buf[0 .. len-1].
+ * Launches nothing; the split is planned for the current device's CU count
+ * and occupancy, or for MI355X's (256 CUs) when no device is present.  Returns TRA_OK, or TRA_ERR_INVALID_ARG for an
  * unknown variant, negative sizes, or buf == NULL with len > 0.
  */
 TRA_API tra_status tra_gemm_describe(int variant, int64_t M, int64_t N, int64_t K,

@@ -82,20 +82,27 @@ def test_describe_plans():
     d = tra.tra_gemm_describe(tra.REGBLOCK_DB, 3072, 3072, 3072)
     assert "grid=2304" in d and "64x64" in d    # 576 large tiles: 2.25 a CU
     assert tra.tra_gemm_describe(tra.AUTO, 16, 16, 16).startswith("variant=auto")
-    # stream-K: 1551 tiles of 64 x 64 on 256 CUs x 2 workgroups leave a last
-    # wave of 15 tiles; their 15 x 96 slices go to 120 workgroups of 12 (an
-    # eighth of a tile each), with two partial tiles of 16 KiB per
-    # workgroup; the main launch adds 4 fixup chunks per shared tile
+    # split in parts: 1551 tiles of 64 x 64 on 256 CUs x 3 workgroups leave
+    # a last wave of 15 tiles, each cut into 8 parts of 12 slices that run in
+    # the main launch (1551 + 15 x 7 workgroups), one partial tile of 16 KiB
+    # per part
     d = tra.tra_gemm_describe(tra.MFMA_STREAMK, 3000, 2049, 1531)
     assert "stream_k_tiles=15" in d and "stream_k_wgs=120" in d
-    assert "workspace_bytes=3932160" in d and "grid=1596" in d
+    assert "workspace_bytes=1966080" in d and "grid=1656" in d
     # whole waves of tiles: no split, no workspace
     d = tra.tra_gemm_describe(tra.MFMA_STREAMK, 4096, 4096, 4096)
     assert "stream_k_tiles=0" in d and "workspace_bytes=0" in d
-    # fewer tiles than a wave: all of them split (40 tiles x 13 slices of 16
-    # over 260 workgroups of at least 2 slices)
+    # fewer tiles than a wave: all of them split, 40 tiles x 13 slices into
+    # 6 parts each (at least 2 slices a part)
     d = tra.tra_gemm_describe(tra.MFMA_STREAMK, 300, 500, 203)
-    assert "stream_k_tiles=40" in d and "stream_k_wgs=260" in d
+    assert "stream_k_tiles=40" in d and "stream_k_wgs=240" in d and "grid=240" in d
+    # stream-K runs: 648 tiles of 256 x 128 on 256 CUs leave 136, more than
+    # half a wave, so their 136 x 256 slices go to 256 workgroups of 136
+    # slices crossing tiles, two partial tiles of 128 KiB per workgroup; the
+    # main launch adds 16 fixup chunks per shared tile (648 + 136 x 15)
+    d = tra.tra_gemm_describe(tra.MFMA_STREAMK, 4608, 4608, 4096)
+    assert "stream_k_tiles=136" in d and "stream_k_wgs=256" in d
+    assert "workspace_bytes=67108864" in d and "grid=2688" in d
     assert "stream_k_tiles=0" in tra.tra_gemm_describe(tra.MFMA, 3000, 2049, 1531)
     with pytest.raises(tra.TraError):
         tra.tra_gemm_describe(7, 1, 1, 1)
@@ -182,7 +189,11 @@ def test_python_matmul_rejects_cpu_tensors():
 def test_workspace_size():
     assert tra.tra_gemm_workspace_size(tra.MFMA, 3000, 2049, 1531) == 0
     assert tra.tra_gemm_workspace_size(tra.NAIVE, 3000, 2049, 1531) == 0
-    assert tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, 3000, 2049, 1531) == 2 * 120 * 64 * 64 * 4
+    # one partial tile per part (120 parts of 64 x 64), or two per stream-K
+    # workgroup (256 workgroups of 256 x 128 tiles)
+    assert tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, 3000, 2049, 1531) == 120 * 64 * 64 * 4
+    assert (tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, 4608, 4608, 4096)
+            == 2 * 256 * 256 * 128 * 4)
     assert tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, 4096, 4096, 4096) == 0
     assert tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, 0, 2049, 1531) == 0
     # K of one slice (16 deep) leaves nothing to split

@@ -34,25 +34,28 @@ def check_tol(C, ref, what):
     assert np.all(err <= TOL * ref.s64), f"{what}: max |diff|/S = {np.max(err / ref.s64):.3e}"
 
 
-# Shapes whose tiles do not fill whole waves, one per tile class (the split
-# each gets on 256 CUs): fewer tiles than a wave (every tile split), a last
-# partial wave of a few tiles split many ways, and the large-tile class.
+# Shapes whose tiles do not fill whole waves, for both forms of the split:
+# parts (the split tiles cut into equal K runs that share the main launch
+# with the data-parallel tiles) and stream-K runs (a launch of their own,
+# runs crossing tiles).  The form each shape gets on MI355X is asserted.
 SPLIT_SHAPES = [
-    (300, 500, 203),      # 40 tiles x 7 slices over 140 workgroups: 3 or 4 partial sums a tile
-    (257, 129, 1000),     # 15 tiles x 32 slices over 120 workgroups: 8 a tile
-    (1500, 1500, 77),     # 576 tiles of 64 x 64: the last 64 over 96 workgroups
-    (3000, 2049, 1531),   # the ragged shape: its last 15 tiles over 120 workgroups
-    (4000, 4200, 203),    # 528 tiles of 256 x 128: the last 16 over 104 workgroups
+    (300, 500, 203, "parts"),     # all 40 tiles in 6 parts of 2-3 slices
+    (257, 129, 1000, "parts"),    # all 15 tiles in 8 parts
+    (3000, 2049, 1531, "parts"),  # the ragged shape: its last 15 tiles in 8 parts
+    (4000, 4200, 203, "parts"),   # 528 tiles of 256 x 128: the last 16 in 6 parts
+    (1500, 1500, 77, "runs"),     # 576 tiles of 64 x 64 in under a wave, 5 slices each
+    (1152, 1152, 8192, "runs"),   # 324 tiles: 2 parts each would leave CUs uneven
+    (4608, 4608, 4096, "runs"),   # 648 tiles of 256 x 128: the last 136, over half a wave
 ]
 
 
-@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "x".join(map(str, s[:3])))
 def test_split_shapes_match_oracle(shape):
     import torch
-    M, N, K = shape
+    M, N, K, form = shape
     d = tra.tra_gemm_describe(tra.MFMA_STREAMK, M, N, K)
-    print(f"[case] stream-K {M}x{N}x{K} ({d})", flush=True)
-    assert "stream_k_tiles=0" not in d
+    print(f"[case] split ({form}) {M}x{N}x{K} ({d})", flush=True)
+    assert "stream_k_tiles=0" not in d and f"split={form} " in d, d
     A = inputs.uniform(M, K, 31)
     B = inputs.uniform(K, N, 32)
     C = tra.matmul(dev(A), dev(B), variant=tra.MFMA_STREAMK)
@@ -140,14 +143,16 @@ def test_auto_uses_the_split_where_it_pays():
 
 
 def test_threads_on_their_own_streams_share_the_library_safely():
-    # four threads, each on its own stream, alternate a small and a large
-    # stream-K shape without synchronising, so the library's per-stream
-    # workspaces are created and grown while the other threads launch; every
-    # result must equal the single-threaded one bit for bit (the split's
-    # reduction order is fixed)
+    # four threads, each on its own stream, alternate a split in parts and
+    # one in stream-K runs (with a larger workspace) without synchronising,
+    # so the library's per-stream workspaces are created and grown while the
+    # other threads launch; every result must equal the single-threaded one
+    # bit for bit (the split's reduction order is fixed)
     import threading
     import torch
-    shapes = [(300, 500, 203), (4000, 4200, 203)]
+    shapes = [(4000, 4200, 203), (1500, 1500, 77)]
+    assert (tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, *shapes[0])
+            < tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, *shapes[1]))
     operands, expect = {}, {}
     for M, N, K in shapes:
         A, B = dev(inputs.uniform(M, K, M + 1)), dev(inputs.uniform(K, N, N + 2))

@@ -32,6 +32,8 @@ struct LaunchPlan {
     int split_k;          // K partitions (1 = none)
     int64_t sk_tiles;     // tiles shared out by K slice (stream-K), 0 = none
     int64_t sk_wgs;       // workgroups that run them
+    const char *split;    // "none", "parts" (K parts in the main launch) or
+                          // "runs" (stream-K runs in a launch of their own)
     size_t workspace_bytes;   // device scratch for partial tiles
 };
 

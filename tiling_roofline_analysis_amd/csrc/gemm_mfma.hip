@@ -58,13 +58,17 @@
 // Workgroup ids are remapped so each of the 8 XCDs runs a compact patch of
 // tiles (shared L2 traffic), in groups of 8 tile rows.
 //
-// Stream-K (gemm_mfma_f32_sk plus the fixup at the start of gemm_mfma_f32):
-// the tiles of the last partial wave are shared out by K slice over up to
-// one wave of workgroups and their partial sums added in K order by a
-// second launch (the decomposition of Osama et al., "Stream-K:
-// Work-centric Parallel Decomposition for Dense Matrix-Matrix
-// Multiplication on the GPU", 2023; the tile count versus CU count
-// trade-off is that of page "Roofline & Tiling notes", key points).
+// Split along K (the tile count versus CU count trade-off of page
+// "Roofline & Tiling notes", key points): the tiles of the last partial
+// wave are shared out by K slice and their partial sums added in K order.
+// Two forms, chosen per shape: when the split tiles fit in half a wave,
+// each is cut into equal parts that run in the same launch as the
+// data-parallel tiles (gemm_mfma_f32_parts, then gemm_mfma_f32_fixup);
+// otherwise runs of slices that may cross tiles go to up to one wave of
+// workgroups in a launch of their own (gemm_mfma_f32_sk, then the fixup at
+// the start of gemm_mfma_f32) -- the decomposition of Osama et al.,
+// "Stream-K: Work-centric Parallel Decomposition for Dense Matrix-Matrix
+// Multiplication on the GPU", 2023.
 #include "gemm_internal.h"
 
 #include <algorithm>
@@ -397,6 +401,27 @@ __host__ __device__ __forceinline__ int sk_slot(const SkPlan &p, int w, int tile
     return 2 * w + (tile == sk_begin(p, w) / static_cast<int>(p.ipt) ? 0 : 1);
 }
 
+// The other form of the split, used when the split tiles fit in half a
+// wave: logical tiles [0, sk_tiles) are each cut into `parts` runs of
+// whole K slices, one workgroup each, that run in the same launch as the
+// data-parallel tiles [sk_tiles, tiles) -- so they fill the CUs that the
+// last wave of whole tiles leaves idle, where stream-K's runs need a
+// launch of their own first.  A part stores its partial sum to workspace
+// slot tile * parts + part; a second, small launch adds each tile's parts
+// in K order.
+struct PartPlan {
+    int64_t ipt;        // K slices per tile, ceil(K / BK)
+    float *ws;          // sk_tiles * parts partial tiles, BM x BN row-major each
+    int tiles_m, tiles_n;
+    int sk_tiles;       // logical tiles split in parts
+    int parts;          // K parts per split tile, 2 .. 8
+};
+
+// First slice of part j of a split tile (parts differ by at most a slice).
+__host__ __device__ __forceinline__ int64_t part_begin(const PartPlan &p, int j) {
+    return static_cast<int64_t>(j) * p.ipt / p.parts;
+}
+
 // One pass of the block tile at (c.m0, c.n0) over slices s0 .. s0+n-1
 // (n = 0: a zero tile).  Stores rows [row_lo, rows) and columns
 // [col_lo, cols) of the tile to `out` (its corner, leading dimension ldo).
@@ -473,6 +498,23 @@ constexpr int fix_chunks() {
     return T::BM * T::BN / 4 / T::THREADS;
 }
 
+// Stores the float4 `s` of a fixup chunk, C[gm][gn .. gn+3], leaving the
+// columns the tile shares with its left neighbour (col < skip_n) and those
+// past N.
+__device__ __forceinline__ void store_chunk(float4 s, float *C, int64_t ldc, int64_t N,
+                                            int64_t gm, int64_t gn, int col, int skip_n,
+                                            int vec_c) {
+    float *cp = C + gm * ldc + gn;
+    if (vec_c && col >= skip_n && (gn & 3) == 0 && gn + 3 < N) {
+        *reinterpret_cast<float4 *>(cp) = s;
+    } else {
+        const float e[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (col + q >= skip_n && gn + q < N) cp[q] = e[q];
+    }
+}
+
 // Adds the partial sums of one chunk of a stream-K tile in K order (so the
 // result does not depend on which workgroup finished first) and stores it
 // to C.  Tiles that a single stream-K workgroup covered were stored by it.
@@ -517,6 +559,33 @@ __device__ __forceinline__ void sk_fixup(int job, int64_t M, int64_t N, float *C
         for (int q = 0; q < 4; ++q)
             if (col + q >= o.skip_n && gn + q < N) cp[q] = e[q];
     }
+}
+
+// The same for a tile split in parts: its parts' partial sums in K order.
+template <class T>
+__device__ __forceinline__ void part_fixup(int job, int64_t M, int64_t N, float *C, int64_t ldc,
+                                           const PartPlan &p, int vec_c) {
+    constexpr int BM = T::BM, BN = T::BN;
+    const int tile = job / fix_chunks<T>();
+    const int f = (job % fix_chunks<T>()) * T::THREADS + static_cast<int>(threadIdx.x);
+    int64_t tm, tn;
+    grouped_tile(tile, p.tiles_m, p.tiles_n, 8, tm, tn);
+    const Origin o = tile_origin<BM, BN>(tm, tn, M, N);
+    const int row = f / (BN / 4), col = 4 * (f % (BN / 4));
+    const int64_t gm = o.m0 + row, gn = o.n0 + col;
+    if (row < o.skip_m || gm >= M) return;
+    const float4 *part = reinterpret_cast<const float4 *>(
+                             p.ws + static_cast<int64_t>(tile) * p.parts * (BM * BN)) + f;
+    float4 s = part[0];
+#pragma unroll 8
+    for (int j = 1; j < p.parts; ++j) {
+        const float4 v = part[static_cast<int64_t>(j) * (BM * BN / 4)];
+        s.x += v.x;
+        s.y += v.y;
+        s.z += v.z;
+        s.w += v.w;
+    }
+    store_chunk(s, C, ldc, N, gm, gn, col, o.skip_n, vec_c);
 }
 
 // The main launch: workgroups [0, sk_tiles * fix_chunks) finish the
@@ -610,6 +679,58 @@ void gemm_mfma_f32_sk(int64_t M, int64_t N, int64_t K,
     }
 }
 
+// The main launch of a split in parts: workgroups [0, sk_tiles * parts)
+// run one K part each and store its partial sum to the workspace, the rest
+// one data-parallel tile each.  (A kernel of its own: its second tile pass
+// in gemm_mfma_f32 would change that kernel's code for every launch.)
+template <class T>
+__global__ __launch_bounds__(T::THREADS)
+void gemm_mfma_f32_parts(int64_t M, int64_t N, int64_t K,
+                         const float *__restrict__ A, int64_t lda,
+                         const float *__restrict__ B, int64_t ldb,
+                         float *__restrict__ C, int64_t ldc, PartPlan p, int vec_a, int vec_b)
+{
+    __shared__ __attribute__((aligned(16))) float lds[T::LDS_WORDS];
+    lds_poison(lds, T::LDS_WORDS);
+
+    const int bid = static_cast<int>(blockIdx.x);
+    const int split = p.sk_tiles * p.parts;
+    int tile, part = -1;
+    if (bid < split) {
+        const int w = static_cast<int>(xcd_remap(bid, split));
+        tile = w / p.parts;
+        part = w - tile * p.parts;
+    } else {
+        const int dp = p.tiles_m * p.tiles_n - p.sk_tiles;
+        tile = p.sk_tiles + static_cast<int>(xcd_remap(bid - split, dp));
+    }
+    int64_t tm, tn;
+    grouped_tile(tile, p.tiles_m, p.tiles_n, 8, tm, tn);
+    const Origin o = tile_origin<T::BM, T::BN>(tm, tn, M, N);
+    const Ctx<T> c{M, N, K, A, lda, B, ldb, o.m0, o.n0, static_cast<int>(threadIdx.x)};
+    if (part >= 0) {                       // a part: the whole block tile to its slot
+        const int64_t s0 = part_begin(p, part);
+        tile_pass<T>(c, vec_a, vec_b, lds, s0, part_begin(p, part + 1) - s0,
+                     p.ws + static_cast<int64_t>(tile * p.parts + part) * (T::BM * T::BN), T::BN,
+                     0, T::BM, 0, T::BN);
+        return;
+    }
+    const int64_t rows = M - o.m0 < T::BM ? M - o.m0 : T::BM;
+    const int64_t cols = N - o.n0 < T::BN ? N - o.n0 : T::BN;
+    tile_pass<T>(c, vec_a, vec_b, lds, 0, p.ipt, C + o.m0 * ldc + o.n0, ldc, o.skip_m, rows,
+                 o.skip_n, cols);
+}
+
+// After gemm_mfma_f32_parts: sk_tiles * fix_chunks workgroups add each
+// split tile's partial sums.
+template <class T>
+__global__ __launch_bounds__(T::THREADS)
+void gemm_mfma_f32_fixup(int64_t M, int64_t N, float *__restrict__ C, int64_t ldc, PartPlan p,
+                         int vec_c)
+{
+    part_fixup<T>(static_cast<int>(blockIdx.x), M, N, C, ldc, p, vec_c);
+}
+
 // Tile shapes (chosen by timing candidates on MI355X, interleaved and
 // repeated on one warm GPU):
 //   Large  256x128x16, 8 waves of 64x64, four register sets: shapes with
@@ -673,15 +794,13 @@ int64_t device_cus() {
     return n;
 }
 
-// Workgroups of the stream-K kernel resident per CU (`fallback`, the value
-// measured on gfx950, if the runtime cannot say).
+// Workgroups of `kernel` resident per CU (`fallback`, the value on gfx950,
+// if the runtime cannot say).
 template <class T>
-int64_t resident_per_cu(int fallback) {
-    static std::atomic<int> cache{0};
+int64_t resident_per_cu(const void *kernel, std::atomic<int> &cache, int fallback) {
     int n = cache.load(std::memory_order_relaxed);
     if (n > 0) return n;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_mfma_f32_sk<T>, T::THREADS, 0) !=
-            hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, T::THREADS, 0) != hipSuccess ||
         n <= 0) {
         (void)hipGetLastError();
         return fallback;
@@ -690,89 +809,161 @@ int64_t resident_per_cu(int fallback) {
     return n;
 }
 
-// Without a device: the stream-K kernel is held at 2 waves per SIMD, so
-// 2 workgroups of 4 waves or 1 of 8 fit a CU when LDS allows.
+// The stream-K kernel (held at no fewer than 2 waves per SIMD): gfx950
+// holds one 8-wave workgroup per CU and three 4-wave ones (129 and 149
+// VGPRs).
 template <class T>
-int resident_fallback() {
-    const int by_waves = 8 / (T::THREADS / 64);
-    const int by_lds = static_cast<int>(160 * 1024 / (T::LDS_WORDS * sizeof(float)));
-    return std::max(1, std::min(by_waves, by_lds));
+int64_t resident_sk() {
+    static std::atomic<int> cache{0};
+    return resident_per_cu<T>(reinterpret_cast<const void *>(gemm_mfma_f32_sk<T>), cache,
+                              T::THREADS == 512 ? 1 : 3);
 }
 
-// The work split of a launch.  Without stream-K, or when the tiles fill
-// whole waves of resident workgroups, every tile is data-parallel.
-// Otherwise the tiles of the last partial wave (all tiles if there are
-// fewer than one wave) are shared out by slice over up to one wave of
-// workgroups, each with at least 2 slices and at least an eighth of a
-// tile's slices, so a tile has at most about 8 partial sums to add.
+// gemm_mfma_f32_parts: gfx950 holds one 8-wave workgroup per CU (over 128
+// VGPRs), and three (four register sets) or four (two) of the 4-wave ones.
 template <class T>
-SkPlan plan_split(int64_t M, int64_t N, int64_t K, bool stream_k) {
-    SkPlan p{};
+int64_t resident_parts() {
+    static std::atomic<int> cache{0};
+    return resident_per_cu<T>(reinterpret_cast<const void *>(gemm_mfma_f32_parts<T>), cache,
+                              T::THREADS == 512 ? 1 : (T::NR == 4 ? 3 : 4));
+}
+
+// The work split of a launch: stream-K runs (sk), or parts (pp.parts > 0),
+// or neither (sk.sk_tiles = 0: every tile data-parallel).
+struct Split {
+    SkPlan sk;
+    PartPlan pp;
+};
+
+// Without stream-K, or when the tiles fill whole waves of resident
+// workgroups, every tile is data-parallel.  Otherwise the tiles of the last
+// partial wave (all tiles if there are fewer than one wave) are split along
+// K:
+//   * in parts, when at least two parts of each fit in one wave of
+//     gemm_mfma_f32_parts and the parts spread evenly over the CUs (at
+//     most one a CU, or no CU more than 10% above the mean): as many parts
+//     as fit, at most 8 and with at least 2 slices each.  (Uneven parts
+//     lose to runs: 1152^2 x 8192, 648 half tiles on 256 CUs, 192 against
+//     188 us.);
+//   * else in stream-K runs over up to one wave of the stream-K kernel,
+//     each with at least 2 slices and at least an eighth of a tile's, so a
+//     tile has at most about 8 partial sums to add.  Whole-tile parts
+//     cannot even out a remainder of more than half a wave: 136 tiles of
+//     256 x 128 left on 256 CUs need about half a tile more per CU, which
+//     runs that cross tiles give (4608^2 x 4096: 1228 us with runs, 1393
+//     with parts).
+template <class T>
+Split plan_split(int64_t M, int64_t N, int64_t K, bool stream_k) {
+    Split r{};
+    SkPlan &p = r.sk;
     const int64_t tiles_m = ceil_div(M, T::BM), tiles_n = ceil_div(N, T::BN);
     const int64_t tiles = tiles_m * tiles_n;
     p.ipt = ceil_div(K, T::BK);
-    if (tiles > kMaxGrid) return p;   // rejected before launch
+    if (tiles > kMaxGrid) return r;   // rejected before launch
     p.tiles_m = static_cast<int>(tiles_m);
     p.tiles_n = static_cast<int>(tiles_n);
-    if (!stream_k || p.ipt < 2) return p;
-    const int64_t slots = device_cus() * resident_per_cu<T>(resident_fallback<T>());
-    if (tiles % slots == 0) return p;
+    if (!stream_k || p.ipt < 2) return r;
+    const int64_t cus = device_cus();
+    const int64_t wave = cus * resident_parts<T>();
+    if (tiles % wave != 0) {
+        const int64_t sk_tiles = tiles % wave;
+        const int64_t parts = std::min<int64_t>({8, p.ipt / 2, wave / sk_tiles});
+        const int64_t n = sk_tiles * parts;
+        if (parts >= 2 && (n <= cus || 10 * ceil_div(n, cus) * cus <= 11 * n)) {
+            p.sk_tiles = static_cast<int>(sk_tiles);
+            r.pp = PartPlan{p.ipt, nullptr, p.tiles_m, p.tiles_n, p.sk_tiles,
+                            static_cast<int>(parts)};
+            return r;
+        }
+    }
+    const int64_t slots = device_cus() * resident_sk<T>();
+    if (tiles % slots == 0) return r;
     const int64_t sk_tiles = tiles % slots;
     const int64_t total = sk_tiles * p.ipt;
-    if (total > (kMaxGrid >> 1)) return p;   // slice arithmetic must fit 32 bits
+    if (total > (kMaxGrid >> 1)) return r;   // slice arithmetic must fit 32 bits
     const int64_t min_slices = std::max<int64_t>(2, ceil_div(p.ipt, 8));
     const int64_t sk_wgs = std::max<int64_t>(1, std::min(slots, total / min_slices));
     p.sk_tiles = static_cast<int>(sk_tiles);
     p.sk_wgs = static_cast<int>(sk_wgs);
     p.q = static_cast<int>(total / sk_wgs);
     p.rm = static_cast<int>(total % sk_wgs);
-    return p;
+    return r;
 }
 
+// Workgroups that run the split: the parts, or the stream-K runs.
+inline int64_t split_wgs(const Split &r) {
+    return r.pp.parts > 0 ? static_cast<int64_t>(r.pp.sk_tiles) * r.pp.parts : r.sk.sk_wgs;
+}
+
+// Partial tiles: one per part, or two per stream-K workgroup.
 template <class T>
-size_t workspace_bytes(const SkPlan &p) {
-    return static_cast<size_t>(2 * p.sk_wgs) * T::BM * T::BN * sizeof(float);
+size_t workspace_bytes(const Split &r) {
+    const size_t slots = static_cast<size_t>(split_wgs(r)) * (r.pp.parts > 0 ? 1 : 2);
+    return slots * T::BM * T::BN * sizeof(float);
+}
+
+// Workgroups of the main launch: every tile, plus the extra parts of the
+// split tiles, or the fixup chunks after the first of each stream-K tile.
+template <class T>
+int64_t main_grid(const Split &r) {
+    const int64_t extra = r.pp.parts > 0 ? r.pp.parts : fix_chunks<T>();
+    return static_cast<int64_t>(r.sk.tiles_m) * r.sk.tiles_n +
+           static_cast<int64_t>(r.sk.sk_tiles) * (extra - 1);
 }
 
 template <class T>
 LaunchPlan plan_for(int64_t M, int64_t N, int64_t K, bool stream_k, const char *name) {
-    const SkPlan s = plan_split<T>(M, N, K, stream_k);
+    const Split r = plan_split<T>(M, N, K, stream_k);
     LaunchPlan p{};
     p.kernel = name;
     p.bm = T::BM;
     p.bn = T::BN;
     p.bk = T::BK;
-    p.grid = ceil_div(M, T::BM) * ceil_div(N, T::BN) +
-             static_cast<int64_t>(s.sk_tiles) * (fix_chunks<T>() - 1);   // the main launch
+    p.grid = main_grid<T>(r);
     p.block = T::THREADS;
     p.lds_bytes = static_cast<int>(T::LDS_WORDS * sizeof(float));
     p.split_k = 1;
-    p.sk_tiles = s.sk_tiles;
-    p.sk_wgs = s.sk_wgs;
-    p.workspace_bytes = workspace_bytes<T>(s);
+    p.sk_tiles = r.sk.sk_tiles;
+    p.sk_wgs = split_wgs(r);
+    p.split = r.pp.parts > 0 ? "parts" : (r.sk.sk_wgs > 0 ? "runs" : "none");
+    p.workspace_bytes = workspace_bytes<T>(r);
     return p;
 }
 
+// Launches on the caller's stream: the stream-K runs and then the main
+// launch (which first adds their partial sums), or the parts with the
+// data-parallel tiles and then their fixup, or the main launch alone.
 template <class T>
 hipError_t launch_tile(const GemmArgs &a, bool stream_k, void *ws, size_t ws_bytes) {
-    SkPlan p = plan_split<T>(a.M, a.N, a.K, stream_k);
-    if (workspace_bytes<T>(p) > ws_bytes || (p.sk_wgs > 0 && ws == nullptr))
+    Split r = plan_split<T>(a.M, a.N, a.K, stream_k);
+    if (workspace_bytes<T>(r) > ws_bytes || (split_wgs(r) > 0 && ws == nullptr))
         return hipErrorInvalidValue;
-    p.ws = static_cast<float *>(ws);
     const int vec_a = vec4_ok(a.A, a.lda), vec_b = vec4_ok(a.B, a.ldb);
+    const int vec_c = vec4_ok(a.C, a.ldc);
+    const dim3 grid(static_cast<uint32_t>(main_grid<T>(r)));
+    hipError_t err;
+    if (r.pp.parts > 0) {
+        PartPlan &p = r.pp;
+        p.ws = static_cast<float *>(ws);
+        hipLaunchKernelGGL(gemm_mfma_f32_parts<T>, grid, dim3(T::THREADS), 0, a.stream, a.M, a.N,
+                           a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, p, vec_a, vec_b);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL(gemm_mfma_f32_fixup<T>,
+                           dim3(static_cast<uint32_t>(p.sk_tiles * fix_chunks<T>())),
+                           dim3(T::THREADS), 0, a.stream, a.M, a.N, a.C, a.ldc, p, vec_c);
+        return hipGetLastError();
+    }
+    SkPlan &p = r.sk;
+    p.ws = static_cast<float *>(ws);
     if (p.sk_wgs > 0) {
         hipLaunchKernelGGL(gemm_mfma_f32_sk<T>, dim3(static_cast<uint32_t>(p.sk_wgs)),
                            dim3(T::THREADS), 0, a.stream, a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb,
                            a.C, a.ldc, p, vec_a, vec_b);
-        const hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
+        if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     // fixups of the stream-K tiles, then the data-parallel tiles
-    const int64_t grid = static_cast<int64_t>(p.tiles_m) * p.tiles_n +
-                         static_cast<int64_t>(p.sk_tiles) * (fix_chunks<T>() - 1);
-    hipLaunchKernelGGL(gemm_mfma_f32<T>, dim3(static_cast<uint32_t>(grid)), dim3(T::THREADS), 0,
-                       a.stream, a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, p, vec_a,
-                       vec_b, static_cast<int>(vec4_ok(a.C, a.ldc)));
+    hipLaunchKernelGGL(gemm_mfma_f32<T>, grid, dim3(T::THREADS), 0, a.stream, a.M, a.N, a.K, a.A,
+                       a.lda, a.B, a.ldb, a.C, a.ldc, p, vec_a, vec_b, vec_c);
     return hipGetLastError();
 }
 
@@ -809,7 +1000,7 @@ LaunchPlan plan_mfma(int64_t M, int64_t N, int64_t K, bool stream_k) {
 //     1500, 1.6%: 313 against 318 us).
 template <class T>
 bool stream_k_pays(int64_t M, int64_t N, int64_t K) {
-    const SkPlan p = plan_split<T>(M, N, K, true);
+    const SkPlan p = plan_split<T>(M, N, K, true).sk;
     if (p.sk_tiles == 0 || p.ipt < 8) return false;
     const int64_t cus = device_cus();
     const int64_t tiles = static_cast<int64_t>(p.tiles_m) * p.tiles_n;

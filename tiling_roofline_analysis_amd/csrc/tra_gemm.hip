@@ -225,12 +225,12 @@ tra_status tra_gemm_describe(int variant, int64_t M, int64_t N, int64_t K, char 
     const tra::LaunchPlan p = plan_rung(rung, M, N, K);
     std::snprintf(buf, len,
                   "variant=%s rung=%s kernel=%s tile=%dx%dx%d grid=%lld block=%d lds_bytes=%d "
-                  "split_k=%d stream_k_tiles=%lld stream_k_wgs=%lld workspace_bytes=%zu",
+                  "split_k=%d stream_k_tiles=%lld stream_k_wgs=%lld split=%s workspace_bytes=%zu",
                   tra_gemm_variant_name(variant),
                   tra_gemm_variant_name(rung), p.kernel, p.bm, p.bn, p.bk,
                   static_cast<long long>(p.grid), p.block, p.lds_bytes, p.split_k,
                   static_cast<long long>(p.sk_tiles), static_cast<long long>(p.sk_wgs),
-                  p.workspace_bytes);
+                  p.split != nullptr ? p.split : "none", p.workspace_bytes);
     return TRA_OK;
 }
 
