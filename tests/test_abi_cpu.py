@@ -239,12 +239,15 @@ def test_caller_workspace_checked_on_host():
     ((300, 500, 203), "mfma"),             # 40 tiles of 7 slices: too short to share
     ((100, 100, 300), "mfma"),             # 4 tiles of 10 slices: saves < 8 us
     ((100, 100, 2000), "mfma_streamk"),    # 4 tiles of 63 slices
-    ((3000, 3000, 1000), "mfma_streamk"),  # 2209 tiles: 8.63 a CU, 4.3% uneven
+    ((3000, 3000, 1000), "mfma"),          # 2209 tiles: 8.63 a CU, 4.3% uneven
+    ((2560, 3328, 1000), "mfma_streamk"),  # 2080 tiles: 8.13 a CU, 10.8% uneven (parts)
+    ((2688, 2752, 1000), "mfma"),          # 1806 tiles: 13.4% uneven, but in stream-K runs
     ((3500, 3500, 1500), "mfma"),          # 3025 tiles: 11.82 a CU, 1.6% uneven
+    ((5000, 5000, 1000), "mfma_streamk"),  # 800 tiles of 256 x 128: 3.13 a CU
     ((8192, 64, 2048), "mfma_streamk"),    # 128 tiles: exactly half the CUs
     ((4096, 128, 2048), "mfma_streamk"),   # 128 tiles
-    ((12288, 64, 2048), "mfma"),           # 192 tiles, 2 GFLOP: too small to split
-    ((768, 768, 1024), "mfma"),            # 144 tiles of 32 slices
+    ((12288, 64, 2048), "mfma"),           # 192 tiles of 128 slices: saves < 8 us
+    ((768, 768, 1024), "mfma"),            # 144 tiles of 64 slices: saves < 8 us
 ])
 def test_auto_choice(shape, rung):
     d = tra.tra_gemm_describe(tra.AUTO, *shape)

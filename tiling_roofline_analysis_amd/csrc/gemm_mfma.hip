@@ -984,27 +984,31 @@ LaunchPlan plan_mfma(int64_t M, int64_t N, int64_t K, bool stream_k) {
     }
 }
 
-// AUTO's choice, from timings of both forms on MI355X.  The split needs K
-// to have at least 8 slices to share out, and then pays
-//   * when at most half the CUs would have a tile and the time that
-//     sharing saves -- (1 - tiles/CUs) of one tile's slices at the
-//     measured per-CU MFMA rate (148 TFLOP/s over 256 CUs) -- covers the
-//     second launch (8 us; 200x300x4100: 20 tiles, 67 -> ~20 us; exactly
-//     half, 8192x64x2048: 128 tiles, 37 -> 29 us);
+// AUTO's choice, from timings of the split against one tile per workgroup
+// on MI355X.  The split needs K to have at least 8 slices to share out,
+// and then pays
+//   * when some CUs would have no tile and the time that sharing saves --
+//     (1 - tiles/CUs) of one tile's slices at the measured per-CU MFMA
+//     rate (148 TFLOP/s over 256 CUs) -- covers the second launch (8 us;
+//     200x300x4100: 20 tiles, 65 -> 18 us; 8192x64x2048: 128 tiles, 34 ->
+//     29 us; not 768x768x1024: 144 tiles, 19 against 22 us);
 //   * otherwise when one tile per workgroup would leave some CUs a whole
-//     tile more work than the mean (at least 4% more: e.g. 2209 tiles on
-//     256 CUs, 8.63 a CU, so some CUs run 9; 3000x3000x1000 165 -> 159 us)
-//     and the product is large enough (>= 4 GFLOP) to hide the second
-//     launch.  Shapes that split evenly over the CUs, like 2304 tiles on
-//     256, stay data-parallel; below 4% the split did not pay (3500x3500x
-//     1500, 1.6%: 313 against 318 us).
+//     tile more work than the mean by at least 10% (split in parts) or 15%
+//     (stream-K runs, which need a launch of their own), and the product
+//     is large enough (>= 4 GFLOP) to hide the second launch.  Measured on
+//     64 x 64 tiles: parts at 3-8% above the mean lost 0-3%, at 10.8%,
+//     11.6% and 15.5% (3000x2049x1531) gained 2%, 3% and 5%; runs up to
+//     13% above the mean lost 1-7%, at 58% (1152^2 x 8192) gained 20%.  On
+//     the large tiles, one workgroup a CU: 11% (6144^2 x 1024) +6%, 28%
+//     (5000^2 x 1000) +21%; runs at 18.5% (4608^2 x 4096) +11%.
 template <class T>
 bool stream_k_pays(int64_t M, int64_t N, int64_t K) {
-    const SkPlan p = plan_split<T>(M, N, K, true).sk;
+    const Split r = plan_split<T>(M, N, K, true);
+    const SkPlan &p = r.sk;
     if (p.sk_tiles == 0 || p.ipt < 8) return false;
     const int64_t cus = device_cus();
     const int64_t tiles = static_cast<int64_t>(p.tiles_m) * p.tiles_n;
-    if (2 * tiles <= cus) {
+    if (tiles < cus) {
         const double slice_s = 2.0 * T::BM * T::BN * T::BK / (148e12 / 256);
         const double saved = (1.0 - static_cast<double>(tiles) / static_cast<double>(cus)) *
                              static_cast<double>(p.ipt) * slice_s;
@@ -1012,8 +1016,9 @@ bool stream_k_pays(int64_t M, int64_t N, int64_t K) {
     }
     if (2.0 * static_cast<double>(M) * static_cast<double>(N) * static_cast<double>(K) < 4e9)
         return false;
-    const int64_t per_cu = ceil_div(tiles, cus);
-    return static_cast<double>(per_cu * cus) >= 1.04 * static_cast<double>(tiles);
+    const double over = static_cast<double>(ceil_div(tiles, cus) * cus) /
+                        static_cast<double>(tiles) - 1.0;
+    return over >= (r.pp.parts > 0 ? 0.10 : 0.15);
 }
 
 bool prefer_stream_k(int64_t M, int64_t N, int64_t K) {
