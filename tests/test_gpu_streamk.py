@@ -46,6 +46,8 @@ SPLIT_SHAPES = [
     (1500, 1500, 77, "runs"),     # 576 tiles of 64 x 64 in under a wave, 5 slices each
     (1152, 1152, 8192, "runs"),   # 324 tiles: 2 parts each would leave CUs uneven
     (4608, 4608, 4096, "runs"),   # 648 tiles of 256 x 128: the last 136, over half a wave
+    (4000, 60, 3000, "parts"),    # narrower than a tile (float4 edge loads), 63 tiles in 8 parts
+    (8200, 61, 3000, "runs"),     # narrower, N odd (element edge loads), 129 tiles
 ]
 
 
