@@ -993,14 +993,16 @@ LaunchPlan plan_mfma(int64_t M, int64_t N, int64_t K, bool stream_k) {
 //     200x300x4100: 20 tiles, 65 -> 18 us; 8192x64x2048: 128 tiles, 34 ->
 //     29 us; not 768x768x1024: 144 tiles, 19 against 22 us);
 //   * otherwise when one tile per workgroup would leave some CUs a whole
-//     tile more work than the mean by at least 10% (split in parts) or 15%
-//     (stream-K runs, which need a launch of their own), and the product
-//     is large enough (>= 4 GFLOP) to hide the second launch.  Measured on
-//     64 x 64 tiles: parts at 3-8% above the mean lost 0-3%, at 10.8%,
-//     11.6% and 15.5% (3000x2049x1531) gained 2%, 3% and 5%; runs up to
-//     13% above the mean lost 1-7%, at 58% (1152^2 x 8192) gained 20%.  On
-//     the large tiles, one workgroup a CU: 11% (6144^2 x 1024) +6%, 28%
-//     (5000^2 x 1000) +21%; runs at 18.5% (4608^2 x 4096) +11%.
+//     tile more work than the mean by at least 10% (split in parts), or by
+//     at least 15% (8-wave tiles) or 25% (4-wave tiles) in stream-K runs,
+//     which need a launch of their own, and the product is large enough
+//     (>= 4 GFLOP) to hide the second launch.  Measured on 64 x 64 tiles:
+//     parts at 3-8% above the mean lost 0-3%, at 10.8%, 11.6% and 15.5%
+//     (3000x2049x1531) gained 2%, 3% and 5%; runs at 5-15% ranged from -5%
+//     to +3%, at 18.5% (2304^2 x 1000) lost 14% and at 58% (1152^2 x 8192)
+//     gained 20%.  On the 8-wave tiles, one workgroup a CU: parts at 11%
+//     (6144^2 x 1024) +6%, 28% (5000^2 x 1000) +21%; runs at 18.5%
+//     (4608^2 x 4096) +11%, 28% (2560^3) +12%.
 template <class T>
 bool stream_k_pays(int64_t M, int64_t N, int64_t K) {
     const Split r = plan_split<T>(M, N, K, true);
@@ -1018,7 +1020,7 @@ bool stream_k_pays(int64_t M, int64_t N, int64_t K) {
         return false;
     const double over = static_cast<double>(ceil_div(tiles, cus) * cus) /
                         static_cast<double>(tiles) - 1.0;
-    return over >= (r.pp.parts > 0 ? 0.10 : 0.15);
+    return over >= (r.pp.parts > 0 ? 0.10 : (T::THREADS == 512 ? 0.15 : 0.25));
 }
 
 bool prefer_stream_k(int64_t M, int64_t N, int64_t K) {
