@@ -851,7 +851,7 @@ struct Split {
 //     cannot even out a remainder of more than half a wave: 136 tiles of
 //     256 x 128 left on 256 CUs need about half a tile more per CU, which
 //     runs that cross tiles give (4608^2 x 4096: 1228 us with runs, 1393
-//     with parts).
+//     unsplit).
 template <class T>
 Split plan_split(int64_t M, int64_t N, int64_t K, bool stream_k) {
     Split r{};
