@@ -444,3 +444,37 @@ def test_non_finite_inputs_propagate(variant, shape):
     C, *_ = run_gpu(variant, A, B)
     same = (C == ref) | (np.isnan(C) & np.isnan(ref))
     assert same.all(), f"{int((~same).sum())} elements differ; first at {np.argwhere(~same)[0]}"
+
+
+def _random_large_shapes(seed, n):
+    # sides drawn around each tile class's range: 64 x 64 tiles (900-3000),
+    # 128 x 128 tiles (about one per CU, 1750-2050) and 256 x 128 tiles
+    # (at least 4 of 128 x 128 per CU, 4100-4700)
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        lo, hi = [(900, 3000), (1750, 2050), (4100, 4700)][i % 3]
+        out.append((int(rng.integers(lo, hi)), int(rng.integers(lo, hi)),
+                    int(rng.integers(40, 700))))
+    return out
+
+
+@pytest.mark.parametrize("variant", [tra.AUTO, tra.MFMA, tra.MFMA_STREAMK],
+                         ids=["auto", "mfma", "mfma_streamk"])
+def test_random_large_shapes_int_patterns_exact(variant):
+    """Seeded random shapes large enough for every tile class and both forms
+    of the K split (parts and stream-K runs), with tails on every axis; on
+    the integer patterns C has period 13 x 7, so every element is checked
+    against the oracle's values on one period, plus a direct sample."""
+    for M, N, K in _random_large_shapes(11, 12):
+        log(f"[case] int patterns {tra.tra_gemm_variant_name(variant)} {M}x{N}x{K} "
+            f"({tra.tra_gemm_describe(variant, M, N, K)})")
+        A, B = int_inputs(M, N, K)
+        C, *_ = run_gpu(variant, A, B)
+        ii, jj = np.meshgrid(np.arange(13), np.arange(7), indexing="ij")
+        T = oracle.gemm_entries(A, B, ii.ravel(), jj.ravel()).c32.reshape(ii.shape)
+        assert_exact(C, T[np.arange(M)[:, None] % 13, np.arange(N)[None, :] % 7],
+                     f"{M}x{N}x{K}")
+        rows, cols = sample_entries(M, N, seed=M + N, n_random=500)
+        assert_exact(C[rows, cols], oracle.gemm_entries(A, B, rows, cols).c32,
+                     f"{M}x{N}x{K} (direct)")
