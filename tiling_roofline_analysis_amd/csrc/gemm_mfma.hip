@@ -665,13 +665,17 @@ void gemm_mfma_f32_sk(int64_t M, int64_t N, int64_t K,
             rows = T::BM;
             cols = T::BN;
         }
-        // The lane id and the operands are laundered per segment: otherwise
-        // the compiler hoists the addresses of all four load modes out of
-        // the segment loop and keeps them live at once (spilling).
+        // The lane id and the leading dimensions are laundered per segment:
+        // otherwise the compiler hoists the addresses of every load mode out
+        // of the segment loop and keeps them live at once (spilling).  The
+        // operand pointers are not: through the asm they lost their global
+        // address space, the loads became flat loads, and the LDS waits
+        // before every barrier then waited for them too -- the whole memory
+        // latency once per slice (1152^2 x 8192: 198 -> 193 us without).
         int lane_id = static_cast<int>(threadIdx.x);
         asm volatile("" : "+v"(lane_id));
         c.t = lane_id;
-        asm volatile("" : "+s"(c.A), "+s"(c.B), "+s"(c.lda), "+s"(c.ldb));
+        asm volatile("" : "+s"(c.lda), "+s"(c.ldb));
         tile_pass<T>(c, vec_a, vec_b, lds, kb, ke - kb, out, ldo, row_lo, rows, col_lo, cols);
         it += ke - kb;
         if (it >= end) break;
@@ -794,24 +798,27 @@ int64_t device_cus() {
     return n;
 }
 
-// Workgroups of `kernel` resident per CU (`fallback`, the value on gfx950,
-// if the runtime cannot say).
+// Workgroups of `kernel` per CU that the split is planned for: `planned`
+// (what gfx950 holds), or fewer if the device's occupancy query says it
+// holds fewer.  (Planning with more than `planned` when a build happens to
+// fit one more workgroup would change which tiles are split, and with it
+// the timings the split's rules were fitted to.)
 template <class T>
-int64_t resident_per_cu(const void *kernel, std::atomic<int> &cache, int fallback) {
+int64_t resident_per_cu(const void *kernel, std::atomic<int> &cache, int planned) {
     int n = cache.load(std::memory_order_relaxed);
     if (n > 0) return n;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, T::THREADS, 0) != hipSuccess ||
         n <= 0) {
         (void)hipGetLastError();
-        return fallback;
+        return planned;
     }
+    n = std::min(n, planned);
     cache.store(n, std::memory_order_relaxed);
     return n;
 }
 
-// The stream-K kernel (held at no fewer than 2 waves per SIMD): gfx950
-// holds one 8-wave workgroup per CU and three 4-wave ones (129 and 149
-// VGPRs).
+// The stream-K kernel (held at no fewer than 2 waves per SIMD): planned
+// at one 8-wave workgroup per CU and three 4-wave ones.
 template <class T>
 int64_t resident_sk() {
     static std::atomic<int> cache{0};
@@ -820,7 +827,8 @@ int64_t resident_sk() {
 }
 
 // gemm_mfma_f32_parts: gfx950 holds one 8-wave workgroup per CU (over 128
-// VGPRs), and three (four register sets) or four (two) of the 4-wave ones.
+// VGPRs), and three (four register sets, 152 VGPRs) or four (two, 128) of
+// the 4-wave ones.
 template <class T>
 int64_t resident_parts() {
     static std::atomic<int> cache{0};
