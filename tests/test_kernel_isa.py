@@ -1,0 +1,89 @@
+"""Static properties of the gfx950 code the kernel sources compile to (host
+only: hipcc emits the device assembly, nothing runs on a GPU).
+
+  * No kernel uses flat memory instructions: every operand lives in global
+    memory or LDS, and a flat load also counts against the LDS wait counter,
+    so a wait for LDS before a barrier would wait for the global loads as
+    well (the stream-K kernel once lost the global address space that way).
+  * No kernel spills to scratch memory.
+  * The MFMA kernels stay within the registers that the split's plans
+    assume: four workgroups of the 64 x 64 tile with two register sets per
+    CU, three with four sets, one of each 8-wave tile (the stream-K kernel:
+    three of either 64 x 64 tile).
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import re
+import subprocess
+
+import pytest
+
+from tiling_roofline_analysis_amd import build
+
+
+def _device_asm(src: str, out_dir: str) -> str:
+    out = os.path.join(out_dir, os.path.splitext(src)[0] + ".s")
+    cmd = [build.hipcc(), *build.FLAGS, "--cuda-device-only", "-S",
+           os.path.join(build.CSRC, src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    with open(out) as fh:
+        return fh.read()
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    d = str(tmp_path_factory.mktemp("isa"))
+    srcs = [s for s in build.SOURCES if s != "tra_gemm.hip"]
+    with cf.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        texts = list(ex.map(lambda s: _device_asm(s, d), srcs))
+    return dict(zip(srcs, texts))
+
+
+def _kernels(text: str):
+    """(name, vgprs, scratch bytes) of every kernel in the metadata."""
+    names = re.findall(r"^\s+\.name:\s+(\S+)", text, re.M)
+    vgprs = [int(x) for x in re.findall(r"^\s+\.vgpr_count:\s+(\d+)", text, re.M)]
+    scratch = [int(x) for x in re.findall(r"^\s+\.private_segment_fixed_size:\s+(\d+)", text,
+                                          re.M)]
+    assert len(names) == len(vgprs) == len(scratch) and names
+    return list(zip(names, vgprs, scratch))
+
+
+def test_no_flat_memory_instructions(asm):
+    for src, text in asm.items():
+        code = "\n".join(line.split(";")[0] for line in text.splitlines())
+        assert not re.search(r"^\s+flat_", code, re.M), f"{src} uses flat memory instructions"
+
+
+def test_no_scratch(asm):
+    for src, text in asm.items():
+        for name, _, scratch in _kernels(text):
+            assert scratch == 0, f"{name} ({src}) spills {scratch} bytes to scratch"
+
+
+# tile (BM, BN, BK, WM, WN, NR) -> largest VGPR count that still gives the
+# planned workgroups per CU (512 VGPRs per SIMD lane; 4 waves per workgroup
+# on the 64 x 64 tile, 8 on the others)
+VGPR_BUDGET = {
+    "64ELi64ELi16ELi32ELi32ELi2": 128,    # four workgroups a CU
+    "64ELi64ELi16ELi32ELi32ELi4": 168,    # three
+    "128ELi128ELi16ELi64ELi32ELi2": 256,  # one
+    "256ELi128ELi16ELi64ELi64ELi4": 256,  # one
+}
+
+
+def test_mfma_register_budgets(asm):
+    seen = set()
+    for name, vgprs, _ in _kernels(asm["gemm_mfma.hip"]):
+        if "gemm_mfma_f32_fixup" in name:
+            continue
+        for key, budget in VGPR_BUDGET.items():
+            if f"MfmaTileILi{key}E" in name:
+                seen.add(key)
+                if "gemm_mfma_f32_sk" in name:
+                    budget = max(budget, 168)    # planned at three a CU
+                assert vgprs <= budget, f"{name}: {vgprs} VGPRs, plan assumes <= {budget}"
+    assert seen == set(VGPR_BUDGET)
