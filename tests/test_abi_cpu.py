@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import tiling_roofline_analysis_amd as tra
@@ -269,3 +270,45 @@ def test_auto_choice(shape, rung):
 def test_auto_tile_class(shape, tile):
     d = tra.tra_gemm_describe(tra.AUTO, *shape)
     assert f"kernel=gemm_mfma_f32{tile} " in d, d
+
+
+def _plan(variant, M, N, K):
+    d = tra.tra_gemm_describe(variant, M, N, K)
+    f = dict(kv.split("=", 1) for kv in d.split() if "=" in kv and not kv.startswith("kernel"))
+    bm, bn, bk = map(int, f["tile"].split("x"))
+    return (bm, bn, bk, int(f["grid"]), int(f["block"]), int(f["stream_k_tiles"]),
+            int(f["stream_k_wgs"]), f["split"], int(f["workspace_bytes"]))
+
+
+def test_split_plans_hold_their_invariants():
+    # over seeded random shapes, the split planned for MI355X's 256 CUs
+    # (planned at 4, 3 and 1 workgroups a CU for parts, 3 and 1 for runs)
+    # keeps the shape of each form: the grid, the workgroups and the
+    # workspace follow from the tile count, and parts cut each split tile
+    # into 2..8 runs of at least 2 slices
+    rng = np.random.default_rng(8)
+    seen = set()
+    for _ in range(400):
+        M, N = (int(x) for x in rng.integers(1, 6000, 2))
+        K = int(rng.choice([rng.integers(1, 64), rng.integers(64, 3000), rng.integers(3000, 20000)]))
+        bm, bn, bk, grid, block, sk, wgs, form, ws = _plan(tra.MFMA_STREAMK, M, N, K)
+        tiles = -(-M // bm) * -(-N // bn)
+        ipt = -(-K // bk)
+        seen.add(form)
+        if form == "none":
+            assert sk == 0 and wgs == 0 and ws == 0 and grid == tiles
+        elif form == "parts":
+            parts = wgs // sk
+            assert wgs == sk * parts and 2 <= parts <= 8 and 2 * parts <= ipt
+            wave = 256 * (1 if block == 512 else (4 if "4 sets" not in
+                                                  tra.tra_gemm_describe(tra.MFMA, M, N, K) else 3))
+            assert sk == tiles % wave and wgs <= wave
+            assert grid == tiles + sk * (parts - 1) and ws == wgs * bm * bn * 4
+        else:
+            assert form == "runs" and 0 < sk <= tiles and 0 < wgs <= 256 * (1 if block == 512 else 3)
+            assert grid == tiles + sk * (bm * bn // 4 // block - 1) and ws == 2 * wgs * bm * bn * 4
+        # the unsplit rung never splits, and AUTO runs one of the two
+        assert "split=none" in tra.tra_gemm_describe(tra.MFMA, M, N, K)
+        auto = tra.tra_gemm_describe(tra.AUTO, M, N, K)
+        assert "rung=mfma " in auto or f"split={form} " in auto
+    assert seen == {"none", "parts", "runs"}
