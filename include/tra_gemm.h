@@ -188,7 +188,7 @@ TRA_API tra_status tra_gemm_workspace_size(int variant, int64_t M, int64_t N, in
  * launch that gemm_f32_variant(variant, M, N, K, ...) would make for
  * 16-byte-aligned operands with lda = K, ldb = N, ldc = N (kernel name, tile
  * shape, grid and block size, the split tiles and the workgroups that run
- * them, the form of the split -- "parts" or "runs", see
+ * them, the form of the split -- "none", "parts" or "runs", see
  * TRA_GEMM_MFMA_STREAMK -- and workspace bytes) into buf[0 .. len-1].
  * Launches nothing; the split is planned for the current device's CU count
  * and occupancy, or for MI355X's (256 CUs) when no device is present.  Returns TRA_OK, or TRA_ERR_INVALID_ARG for an
