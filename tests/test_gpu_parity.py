@@ -310,6 +310,67 @@ def test_strides_and_alignment(variant, shape, layout):
     assert np.all(buf[:off] == C_SENTINEL)
 
 
+# --- element offsets past 2^31 ------------------------------------------------
+# Rows of 65536 floats: 40000 of them span 2.6e9 elements (10.5 GB), so the
+# last rows of the strided operand start beyond element 2^31 (byte 2^33).
+# An index or offset kept in 32 bits would read or write the wrong place.
+HUGE_LD = 65536
+
+
+def strided_on_device(x: np.ndarray, ld: int):
+    """Device buffer of rows x ld floats holding x in its first columns, the
+    four words after each row set to C_SENTINEL; returns (buffer, view)."""
+    import torch
+    rows, cols = x.shape
+    buf = torch.empty(rows * ld, dtype=torch.float32, device="cuda:0")
+    view = buf.view(rows, ld)
+    view[:, cols:cols + 4].fill_(float(C_SENTINEL))
+    view[:, :cols].copy_(torch.from_numpy(x))
+    return buf, view
+
+
+@pytest.mark.parametrize("case", ["A_and_C_rows", "B_rows"])
+@pytest.mark.parametrize("variant", RUNGS + [tra.AUTO], ids=RUNG_IDS + ["auto"])
+def test_offsets_past_2_31_elements(variant, case):
+    import torch
+    if case == "A_and_C_rows":
+        M, N, K = 40000, 64, 64
+    else:
+        M, N, K = 64, 64, 40000
+    A, B = int_inputs(M, N, K)
+    ref = oracle.gemm(A, B)
+    log(f"offsets past 2^31: {case} {M}x{N}x{K} variant {variant}")
+    keep = []   # the device buffers, freed at the end
+    if case == "A_and_C_rows":
+        bufA, vA = strided_on_device(A, HUGE_LD)
+        tB = torch.from_numpy(B).to("cuda:0")
+        bufC, vC = strided_on_device(np.zeros((M, N), np.float32), HUGE_LD)
+        vC[:, :N].fill_(float(C_SENTINEL))
+        keep += [bufA, tB, bufC]
+        args = (vA.data_ptr(), HUGE_LD, tB.data_ptr(), N, vC.data_ptr(), HUGE_LD)
+        assert (M - 1) * HUGE_LD > 2 ** 31
+    else:
+        tA = torch.from_numpy(A).to("cuda:0")
+        bufB, vB = strided_on_device(B, HUGE_LD)
+        vC = torch.full((M, N), float(C_SENTINEL), dtype=torch.float32, device="cuda:0")
+        keep += [tA, bufB, vC]
+        args = (tA.data_ptr(), K, vB.data_ptr(), HUGE_LD, vC.data_ptr(), N)
+        assert (K - 1) * HUGE_LD > 2 ** 31
+    st = tra.gemm_f32_variant(variant, M, N, K, *args, torch.cuda.current_stream().cuda_stream)
+    assert st == tra.TRA_OK, tra.tra_status_string(st)
+    torch.cuda.synchronize()
+    C = vC[:, :N].cpu().numpy()
+    tail_ok = case != "A_and_C_rows" or bool(torch.all(vC[:, N:N + 4] == float(C_SENTINEL)))
+    del keep, vC
+    if case == "A_and_C_rows":
+        del bufA, vA, bufC
+    else:
+        del bufB, vB
+    torch.cuda.empty_cache()
+    assert_exact(C, ref.c32, f"{case} variant {variant}")
+    assert tail_ok, "a word after a row of C was written"
+
+
 @pytest.mark.parametrize("variant", RUNGS, ids=RUNG_IDS)
 def test_k_zero_writes_zeros(variant):
     A = np.zeros((70, 0), np.float32)
