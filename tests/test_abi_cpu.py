@@ -312,3 +312,19 @@ def test_split_plans_hold_their_invariants():
         auto = tra.tra_gemm_describe(tra.AUTO, M, N, K)
         assert "rung=mfma " in auto or f"split={form} " in auto
     assert seen == {"none", "parts", "runs"}
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    # no CPU fallback: with the library absent, every call raises before it
+    # does anything
+    monkeypatch.setattr(tra, "LIB_PATH", str(tmp_path / "libtra_gemm.so"))
+    monkeypatch.setattr(tra, "_lib", None)
+    calls = (lambda: tra.load(),
+             lambda: tra.gemm_f32(4, 4, 4, 0, 4, 0, 4, 0, 4),
+             lambda: tra.gemm_f32_variant(tra.MFMA, 4, 4, 4, 0, 4, 0, 4, 0, 4),
+             lambda: tra.tra_gemm_describe(tra.AUTO, 4, 4, 4),
+             lambda: tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, 4, 4, 4))
+    for call in calls:
+        with pytest.raises(RuntimeError, match="is not built"):
+            call()
+    assert tra._lib is None
