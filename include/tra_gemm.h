@@ -23,12 +23,19 @@
  * Only the stream-K variant needs device scratch (partial tiles, see
  * TRA_GEMM_MFMA_STREAMK): gemm_f32_variant_ws takes it from the caller and
  * allocates nothing; gemm_f32 and gemm_f32_variant use a workspace that the
- * library allocates on first need for each (device, stream) pair and keeps
- * until the process ends (it grows, after synchronising that stream, when a
- * later call needs more).  The pair is keyed by the stream's handle, and
- * calls on one handle rely on the stream's order: synchronise a stream that
- * has such calls in flight before destroying it, since a stream created
- * later may be given the same handle.
+ * library allocates on first need for each (device, stream) pair -- for
+ * hipStreamPerThread, for each (device, thread) -- and keeps until
+ * tra_gemm_release_workspaces() or the end of the process.  When a call
+ * needs more, the buffer grows in stream order (hipFreeAsync of the old one
+ * and hipMallocAsync of the new one, both on `stream`): nothing waits on
+ * the host, and calls on different streams never wait for each other.
+ * The pair is keyed by the stream's handle, and calls on one handle rely on
+ * the stream's order: synchronise a stream that has such calls in flight
+ * before destroying it, since a stream created later may be given the same
+ * handle.  While `stream` is being captured into a graph these two entry
+ * points refuse a call that needs scratch (TRA_ERR_UNSUPPORTED): capture
+ * takes gemm_f32_variant_ws, whose buffer the caller keeps alive for as
+ * long as the graph.
  *
  * Asynchrony: gemm_f32 and gemm_f32_variant return once the kernels are
  * enqueued on `stream` (a hipStream_t; NULL means the null stream of the
@@ -134,9 +141,10 @@ typedef enum tra_gemm_variant {
  *
  * Returns TRA_OK, TRA_ERR_INVALID_ARG (negative size, ld too small, NULL
  * pointer where data is needed, C overlapping A or B), TRA_ERR_UNSUPPORTED
- * (the launch grid would exceed 2^31 - 1 workgroups) or TRA_ERR_HIP (a
- * launch failed, or the library's stream-K workspace could not be
- * allocated).
+ * (the launch grid would exceed 2^31 - 1 workgroups or 2^32 - 1 lanes, or
+ * the call needs the library's scratch while `stream` is being captured) or
+ * TRA_ERR_HIP (a launch failed, or the library's stream-K workspace could
+ * not be allocated).
  */
 TRA_API tra_status gemm_f32(int64_t M, int64_t N, int64_t K,
                     const float *A, int64_t lda,
@@ -233,6 +241,18 @@ TRA_API double tra_probe_work(int probe, int64_t amount);
 TRA_API tra_status tra_probe_copy_f32(int64_t n, const float *src, float *dst, void *stream);
 TRA_API tra_status tra_probe_mfma_f32(int64_t iters, float *sink, void *stream);
 TRA_API tra_status tra_probe_fma_f32(int64_t iters, float *sink, void *stream);
+
+/*
+ * tra_gemm_release_workspaces: frees every workspace that gemm_f32 and
+ * gemm_f32_variant allocated (on every device and stream), for a caller
+ * about to unload the library or to hand the memory back.  It first waits
+ * for all work on each such device (hipDeviceSynchronize), since the
+ * streams the buffers served may no longer exist.  Later calls allocate
+ * again as needed.  Returns TRA_OK, or TRA_ERR_HIP (kept for
+ * tra_last_hip_error()) if a wait or release failed; the current device is
+ * restored either way.
+ */
+TRA_API tra_status tra_gemm_release_workspaces(void);
 
 /* Static strings for a status or variant value ("unknown" otherwise). */
 TRA_API const char *tra_status_string(int status);

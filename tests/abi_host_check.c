@@ -3,7 +3,8 @@
  * AddressSanitizer and UndefinedBehaviorSanitizer by
  * tests/test_host_sanitizers.py.  Every call here is answered on the host:
  * names, plans (tra_gemm_describe into buffers of every small length),
- * workspace sizes, and calls rejected by the argument checks.  Nothing is
+ * workspace sizes, calls rejected by the argument checks, and the release
+ * of workspaces when none was allocated.  Nothing is
  * launched, so no GPU is needed.  Exits 0 and prints "ok" when every
  * result is as the header documents.
  */
@@ -68,8 +69,13 @@ int main(void) {
     CHECK(gemm_f32_variant(42, 4, 4, 4, A, 4, B, 4, C, 4, NULL) == TRA_ERR_INVALID_ARG);
     CHECK(gemm_f32_variant_ws(TRA_GEMM_MFMA_STREAMK, 3000, 2049, 1531, A, 1531, B, 2049, C,
                               2049, NULL, 1, NULL) == TRA_ERR_INVALID_ARG);
+    /* 2^24 workgroups of 256 lanes: 2^32 lanes, past HIP's limit */
+    CHECK(gemm_f32_variant(TRA_GEMM_NAIVE, (int64_t)1 << 26, 64, 0, NULL, 0, NULL, 64, C, 64,
+                           NULL) == TRA_ERR_UNSUPPORTED);
     /* nothing to compute: OK, no launch */
     CHECK(gemm_f32(0, 4, 4, NULL, 4, NULL, 4, NULL, 4, NULL) == TRA_OK);
+    /* no workspace was allocated: nothing to release */
+    CHECK(tra_gemm_release_workspaces() == TRA_OK);
     printf("ok\n");
     return 0;
 }

@@ -152,6 +152,21 @@ def test_grid_too_large_is_unsupported():
     assert st == tra.TRA_ERR_UNSUPPORTED
 
 
+def test_lane_count_past_32_bits_is_unsupported():
+    # HIP needs grid x block below 2^32 in the x dimension: the naive rung
+    # (256 lanes a workgroup) at 2^26 x 64 needs 2^24 workgroups, under the
+    # workgroup limit but 2^32 lanes
+    M = 1 << 26
+    assert "grid=16777216 block=256" in tra.tra_gemm_describe(tra.NAIVE, M, 64, 0)
+    st = tra.gemm_f32_variant(tra.NAIVE, M, 64, 0, None, 0, None, 64, C_ADDR, 64, None)
+    assert st == tra.TRA_ERR_UNSUPPORTED
+
+
+def test_release_without_workspaces_touches_nothing():
+    # nothing was allocated in this process: OK without any HIP call
+    assert tra.tra_gemm_release_workspaces() == tra.TRA_OK
+
+
 @pytest.mark.parametrize("M,N", [(0, 5), (5, 0), (0, 0)])
 def test_empty_output_is_noop(M, N):
     # nothing to compute: OK without touching any pointer (all NULL here)
@@ -185,6 +200,34 @@ def test_python_matmul_rejects_cpu_tensors():
     import torch
     with pytest.raises(TypeError):
         tra.matmul(torch.zeros(2, 2), torch.zeros(2, 2))
+
+
+def test_python_layout_check():
+    # the leading dimension the binding passes for a view, or a refusal for
+    # a view that is not row-major
+    import torch
+    base = torch.zeros(4, 8)
+    ld = tra._row_major_ld
+    assert ld(tuple(base.shape), base.stride(), "A") == 8
+    assert ld(tuple(base[1:3, 2:7].shape), base[1:3, 2:7].stride(), "A") == 8
+    assert ld(tuple(base[:1].shape), base[:1].stride(), "A") == 8
+    assert ld(tuple(base[:, :1].shape), base[:, :1].stride(), "A") == 8
+    assert ld((0, 5), (5, 1), "A") == 5
+    # one row with every other element: not contiguous, refused (it used to
+    # be passed as a dense row of 4)
+    v = base[:1, ::2]
+    assert tuple(v.shape) == (1, 4) and v.stride() == (8, 2)
+    with pytest.raises(ValueError, match="unit column stride"):
+        ld(tuple(v.shape), v.stride(), "A")
+    with pytest.raises(ValueError, match="unit column stride"):
+        ld(tuple(base.t().shape), base.t().stride(), "B")
+    # rows that overlap (a broadcast view) are refused too
+    e = torch.zeros(1, 3).expand(4, 3)
+    with pytest.raises(ValueError, match="row stride"):
+        ld(tuple(e.shape), e.stride(), "C")
+    e1 = torch.zeros(1, 1).expand(4, 1)
+    with pytest.raises(ValueError, match="row stride"):
+        ld(tuple(e1.shape), e1.stride(), "C")
 
 
 def test_workspace_size():

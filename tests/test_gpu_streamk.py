@@ -185,3 +185,122 @@ def test_threads_on_their_own_streams_share_the_library_safely():
     assert not failures, failures
     for key, C in outs.items():
         assert torch.equal(C, expect[plan[key]]), key
+
+
+def _hip_runtime():
+    """The process's HIP runtime (the copy torch loaded), for stream calls
+    torch does not expose: creating and destroying raw streams."""
+    import ctypes
+    import torch  # noqa: F401  (loads the runtime first)
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipStreamCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    hip.hipStreamSynchronize.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+def _int_case(M, N, K):
+    A, B = inputs.int_pattern_a(M, K), inputs.int_pattern_b(K, N)
+    ii, jj = np.meshgrid(np.arange(min(13, M)), np.arange(min(7, N)), indexing="ij")
+    per = oracle.gemm_entries(A, B, ii.ravel(), jj.ravel()).c32.reshape(ii.shape)
+    exp = per[np.arange(M)[:, None] % 13, np.arange(N)[None, :] % 7]
+    return dev(A), dev(B), exp
+
+
+def test_streams_destroyed_and_recreated_between_split_calls():
+    # raw streams created and destroyed around each split call (synchronised
+    # first, as the header asks); handles of destroyed streams are commonly
+    # handed out again, and the buffer of a handle must then grow in stream
+    # order on the new stream
+    import ctypes
+    import torch
+    hip = _hip_runtime()
+    small, large = (300, 500, 203), (4000, 4200, 203)
+    cases = {s: _int_case(*s) for s in (small, large)}
+    handles = []
+    for i, shape in enumerate((small, large, small, large, large, small)):
+        h = ctypes.c_void_p()
+        assert hip.hipStreamCreate(ctypes.byref(h)) == 0
+        handles.append(h.value)
+        A, B, exp = cases[shape]
+        M, N, K = shape
+        C = torch.full((M, N), float("nan"), device="cuda:0")
+        torch.cuda.synchronize()
+        st = tra.gemm_f32_variant(tra.MFMA_STREAMK, M, N, K, A.data_ptr(), K, B.data_ptr(), N,
+                                  C.data_ptr(), N, h.value)
+        assert st == tra.TRA_OK, tra.tra_status_string(st)
+        assert hip.hipStreamSynchronize(h) == 0
+        assert hip.hipStreamDestroy(h) == 0
+        assert np.array_equal(C.cpu().numpy(), exp), (i, shape)
+    print(f"[case] stream handles used: {len(set(handles))} distinct of {len(handles)}",
+          flush=True)
+
+
+def test_per_thread_default_stream_keeps_one_workspace_per_thread():
+    # hipStreamPerThread is one handle naming a different stream in each
+    # thread: each thread must get its own buffer.  Four threads alternate
+    # a small and a large split on it without synchronising in between.
+    import threading
+    import torch
+    hip = _hip_runtime()
+    per_thread = 2   # hipStreamPerThread
+    shapes = [(300, 500, 203), (4000, 4200, 203)]
+    cases = {s: _int_case(*s) for s in shapes}
+    outs = {(t, i): torch.full(shapes[(t + i) % 2][:2], float("nan"), device="cuda:0")
+            for t in range(4) for i in range(4)}
+    torch.cuda.synchronize()
+    failures = []
+
+    def work(t):
+        for i in range(4):
+            M, N, K = shapes[(t + i) % 2]
+            A, B, _ = cases[(M, N, K)]
+            st = tra.gemm_f32_variant(tra.MFMA_STREAMK, M, N, K, A.data_ptr(), K,
+                                      B.data_ptr(), N, outs[(t, i)].data_ptr(), N, per_thread)
+            if st != tra.TRA_OK:
+                failures.append((t, i, tra.tra_status_string(st)))
+        if hip.hipStreamSynchronize(per_thread) != 0:
+            failures.append((t, "sync"))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not failures, failures
+    for (t, i), C in outs.items():
+        assert np.array_equal(C.cpu().numpy(), cases[shapes[(t + i) % 2]][2]), (t, i)
+
+
+def test_graph_capture_takes_the_caller_workspace():
+    # while a stream is captured, the library's own scratch is refused (it
+    # would be allocated into the graph); the caller's workspace is
+    # captured, and every replay -- with eager work and synchronisation in
+    # between -- equals the eager result
+    import torch
+    M, N, K = 3000, 2049, 1531
+    A, B = dev(inputs.uniform(M, K, 7)), dev(inputs.uniform(K, N, 8))
+    need = tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, M, N, K)
+    ws = torch.empty(need // 4, device="cuda:0")
+    eager = tra.matmul(A, B, variant=tra.MFMA_STREAMK, workspace=ws).clone()
+    C = torch.full((M, N), float("nan"), device="cuda:0")
+    other = torch.empty((M, N), device="cuda:0")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        refused = tra.gemm_f32_variant(tra.MFMA_STREAMK, M, N, K, A.data_ptr(), K, B.data_ptr(),
+                                       N, C.data_ptr(), N, s.cuda_stream)
+        st = tra.gemm_f32_variant_ws(tra.MFMA_STREAMK, M, N, K, A.data_ptr(), K, B.data_ptr(), N,
+                                     C.data_ptr(), N, ws.data_ptr(), need, s.cuda_stream)
+    assert refused == tra.TRA_ERR_UNSUPPORTED
+    assert st == tra.TRA_OK
+    for r in range(3):
+        C.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(C, eager), r
+        tra.matmul(A, B, other)   # eager work between replays (library workspace)
+        torch.cuda.synchronize()

@@ -43,7 +43,8 @@ VARIANTS = {"auto": AUTO, "naive": NAIVE, "lds_tiled": LDS_TILED,
 LADDER = (NAIVE, LDS_TILED, REGBLOCK_DB, MFMA)
 
 ABI_FUNCTIONS = ("gemm_f32", "gemm_f32_variant", "gemm_f32_variant_ws",
-                 "tra_gemm_workspace_size", "tra_gemm_describe", "tra_status_string",
+                 "tra_gemm_workspace_size", "tra_gemm_release_workspaces",
+                 "tra_gemm_describe", "tra_status_string",
                  "tra_gemm_variant_name", "tra_last_hip_error", "tra_probe_work",
                  "tra_probe_copy_f32", "tra_probe_mfma_f32", "tra_probe_fma_f32")
 
@@ -108,6 +109,8 @@ def _open(path: str) -> ctypes.CDLL:
     lib.tra_gemm_workspace_size.argtypes = [c_int, i64, i64, i64,
                                             ctypes.POINTER(ctypes.c_size_t)]
     lib.tra_gemm_workspace_size.restype = c_int
+    lib.tra_gemm_release_workspaces.argtypes = []
+    lib.tra_gemm_release_workspaces.restype = c_int
     lib.tra_gemm_describe.argtypes = [c_int, i64, i64, i64, ctypes.c_char_p, ctypes.c_size_t]
     lib.tra_gemm_describe.restype = c_int
     lib.tra_status_string.argtypes = [c_int]
@@ -151,6 +154,10 @@ def tra_gemm_workspace_size(variant: int, M: int, N: int, K: int) -> int:
     return out.value
 
 
+def tra_gemm_release_workspaces() -> int:
+    return load().tra_gemm_release_workspaces()
+
+
 def tra_gemm_describe(variant: int, M: int, N: int, K: int) -> str:
     buf = ctypes.create_string_buffer(256)
     st = load().tra_gemm_describe(variant, M, N, K, buf, len(buf))
@@ -189,18 +196,28 @@ def tra_probe_fma_f32(iters, sink, stream=None) -> int:
 
 # --- torch convenience --------------------------------------------------------
 
-def _check_operand(x, name):
+def _row_major_ld(shape, strides, name) -> int:
+    """Leading dimension of a 2-D row-major view with this shape and these
+    strides (in elements), or ValueError if the view is not row-major:
+    every row must be contiguous, whatever the row count (a one-row view
+    with a column stride above 1 is not a row-major matrix either), and
+    rows may not overlap."""
+    rows, cols = shape
+    if cols > 1 and strides[1] != 1:
+        raise ValueError(f"{name} must be row-major (unit column stride)")
+    if rows > 1 and strides[0] < max(1, cols):
+        raise ValueError(f"{name} must be row-major (row stride at least the row length)")
+    return strides[0] if rows > 1 else max(1, cols)
+
+
+def _check_operand(x, name) -> int:
+    """Checks a matmul operand and returns its leading dimension."""
     import torch
     if not isinstance(x, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if x.dtype != torch.float32 or x.dim() != 2 or not x.is_cuda:
         raise TypeError(f"{name} must be a 2-D float32 tensor on a GPU")
-    if x.size(0) > 1 and x.size(1) > 0 and x.stride(1) != 1:
-        raise ValueError(f"{name} must be row-major (unit column stride)")
-
-
-def _ld(x) -> int:
-    return x.stride(0) if x.size(0) > 1 else max(1, x.size(1))
+    return _row_major_ld(tuple(x.shape), x.stride(), name)
 
 
 def matmul(A, B, C=None, variant: int = AUTO, stream=None, workspace=None):
@@ -214,30 +231,29 @@ def matmul(A, B, C=None, variant: int = AUTO, stream=None, workspace=None):
     scratch for the stream-K variant.
     """
     import torch
-    _check_operand(A, "A")
-    _check_operand(B, "B")
+    lda = _check_operand(A, "A")
+    ldb = _check_operand(B, "B")
     M, K = A.shape
     if B.shape[0] != K:
         raise ValueError(f"inner dimensions differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
     N = B.shape[1]
     if C is None:
         C = torch.empty((M, N), dtype=torch.float32, device=A.device)
-    else:
-        _check_operand(C, "C")
-        if tuple(C.shape) != (M, N):
-            raise ValueError(f"C must be {M} x {N}")
+    ldc = _check_operand(C, "C")
+    if tuple(C.shape) != (M, N):
+        raise ValueError(f"C must be {M} x {N}")
     if B.device != A.device or C.device != A.device:
         raise ValueError("A, B and C must be on the same device")
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
     with torch.cuda.device(A.device):
         if workspace is None:
-            st = gemm_f32_variant(variant, M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B),
-                                  C.data_ptr(), _ld(C), s.cuda_stream)
+            st = gemm_f32_variant(variant, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
+                                  C.data_ptr(), ldc, s.cuda_stream)
         else:
             if not workspace.is_cuda or workspace.device != A.device or not workspace.is_contiguous():
                 raise ValueError("workspace must be a contiguous tensor on A's device")
-            st = gemm_f32_variant_ws(variant, M, N, K, A.data_ptr(), _ld(A), B.data_ptr(),
-                                     _ld(B), C.data_ptr(), _ld(C), workspace.data_ptr(),
+            st = gemm_f32_variant_ws(variant, M, N, K, A.data_ptr(), lda, B.data_ptr(),
+                                     ldb, C.data_ptr(), ldc, workspace.data_ptr(),
                                      workspace.numel() * workspace.element_size(), s.cuda_stream)
     if st != TRA_OK:
         raise TraError(st, "gemm_f32_variant")

@@ -29,7 +29,6 @@ struct LaunchPlan {
     int64_t grid;         // workgroups
     int block;            // lanes per workgroup
     int lds_bytes;        // LDS per workgroup
-    int split_k;          // K partitions (1 = none)
     int64_t sk_tiles;     // tiles shared out by K slice (stream-K), 0 = none
     int64_t sk_wgs;       // workgroups that run them
     const char *split;    // "none", "parts" (K parts in the main launch) or
@@ -37,8 +36,11 @@ struct LaunchPlan {
     size_t workspace_bytes;   // device scratch for partial tiles
 };
 
-// Grid limit of one launch (workgroups in the x dimension).
+// Limits of one launch: workgroups in the x dimension (the kernels index
+// them with int), and work-items in the x dimension, which HIP requires to
+// fit 32 bits (grid x block <= 2^32 - 1).
 constexpr int64_t kMaxGrid = 2147483647;
+constexpr int64_t kMaxGridLanes = 4294967295;
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -71,7 +71,6 @@ LaunchPlan plan_lds_tiled(int64_t M, int64_t N, int64_t /*K*/) {
     p.grid = ceil_div(M, kTile) * ceil_div(N, kTile);
     p.block = kTile * kTile;
     p.lds_bytes = 2 * kTile * kTile * static_cast<int>(sizeof(float));
-    p.split_k = 1;
     return p;
 }
 

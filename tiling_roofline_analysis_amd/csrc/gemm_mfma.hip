@@ -930,7 +930,6 @@ LaunchPlan plan_for(int64_t M, int64_t N, int64_t K, bool stream_k, const char *
     p.grid = main_grid<T>(r);
     p.block = T::THREADS;
     p.lds_bytes = static_cast<int>(T::LDS_WORDS * sizeof(float));
-    p.split_k = 1;
     p.sk_tiles = r.sk.sk_tiles;
     p.sk_wgs = split_wgs(r);
     p.split = r.pp.parts > 0 ? "parts" : (r.sk.sk_wgs > 0 ? "runs" : "none");

@@ -49,7 +49,6 @@ LaunchPlan plan_naive(int64_t M, int64_t N, int64_t /*K*/) {
     p.grid = ceil_div(M, kNaiveRows) * ceil_div(N, kNaiveCols);
     p.block = kNaiveCols * kNaiveRows;
     p.lds_bytes = 0;
-    p.split_k = 1;
     return p;
 }
 

@@ -279,7 +279,6 @@ LaunchPlan plan_reg(int64_t M, int64_t N, const char *name) {
     p.grid = ceil_div(M, T::BM) * ceil_div(N, T::BN);
     p.block = T::THREADS;
     p.lds_bytes = static_cast<int>(2 * (T::BM * T::AST + T::BK * T::BST) * sizeof(float));
-    p.split_k = 1;
     return p;
 }
 

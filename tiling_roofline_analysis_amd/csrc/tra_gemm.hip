@@ -15,7 +15,9 @@
 
 #include <cstdio>
 #include <cstring>
+#include <memory>
 #include <mutex>
+#include <thread>
 #include <vector>
 
 #include "gemm_internal.h"
@@ -64,52 +66,77 @@ tra::LaunchPlan plan_rung(int rung, int64_t M, int64_t N, int64_t K) {
     }
 }
 
-// The library's own workspaces, one per (device, stream) pair.  Work on one
-// stream runs in order, so calls on that stream may share one buffer; a
-// buffer is only replaced (by a larger one) after its stream has drained.
-// Keyed by the stream handle: a stream destroyed with calls in flight and a
-// new stream given its handle would share the buffer unordered, so the
-// header asks callers to synchronise a stream before destroying it.
-// (Ordering each use by an event instead cost 1-11% on the stream-K
-// shapes: a stream waiting on its own event is not free.)
-// The mutex is held from the lookup until the kernels are enqueued, so a
-// replacement cannot free a buffer another thread is about to launch with.
+// The library's own workspaces, one per (device, stream) pair -- and per
+// thread for hipStreamPerThread, a single handle that names a different
+// stream in every thread.  Work on one stream runs in order, so calls on
+// that stream may share one buffer.
+//
+// Growth is stream-ordered and never waits on the host: the old buffer is
+// released with hipFreeAsync and the larger one taken with hipMallocAsync,
+// both enqueued on the stream itself, so the release happens after every
+// kernel already enqueued there has finished with the old buffer.
+//
+// Locking: g_ws_list_mutex guards only the list (held while an entry is
+// found or added).  Each entry has its own mutex, held from the size check
+// until the call's kernels are enqueued, so that another thread on the same
+// stream cannot release the buffer between the two; calls on different
+// streams never wait for each other.
+//
+// Entries are keyed by the stream handle: a stream destroyed with such calls
+// still in flight, whose handle a later stream receives, would share the
+// buffer with them unordered -- so a stream with split calls in flight must
+// be synchronised before it is destroyed.  Buffers live until
+// tra_gemm_release_workspaces() or the end of the process.
 struct LibWorkspace {
     int device;
     hipStream_t stream;
-    void *ptr;
-    size_t bytes;
+    std::thread::id thread;   // set only for hipStreamPerThread
+    std::mutex mutex;         // held across one call's size check and enqueue
+    void *ptr = nullptr;
+    size_t bytes = 0;
 };
-std::mutex g_ws_mutex;
-std::vector<LibWorkspace> g_ws;
+std::mutex g_ws_list_mutex;
+std::vector<std::unique_ptr<LibWorkspace>> g_ws;
 
-// Finds or grows the workspace of (current device, stream); caller holds
-// g_ws_mutex.
-hipError_t library_workspace(hipStream_t stream, size_t bytes, void **out) {
+// The entry of (current device, stream[, thread]), created on first use.
+hipError_t find_workspace(hipStream_t stream, LibWorkspace **out) {
     int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
+    const hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
-    for (LibWorkspace &w : g_ws) {
-        if (w.device != dev || w.stream != stream) continue;
-        if (w.bytes >= bytes) {
-            *out = w.ptr;
+    const std::thread::id thread =
+        stream == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id();
+    std::lock_guard<std::mutex> lock(g_ws_list_mutex);
+    for (const auto &w : g_ws) {
+        if (w->device == dev && w->stream == stream && w->thread == thread) {
+            *out = w.get();
             return hipSuccess;
         }
-        if ((err = hipStreamSynchronize(stream)) != hipSuccess) return err;
-        if ((err = hipFree(w.ptr)) != hipSuccess) return err;
+    }
+    auto w = std::make_unique<LibWorkspace>();
+    w->device = dev;
+    w->stream = stream;
+    w->thread = thread;
+    *out = w.get();
+    g_ws.push_back(std::move(w));
+    return hipSuccess;
+}
+
+// Makes w hold at least `bytes` (rounded up to 1 MiB), in stream order;
+// the caller holds w->mutex.
+hipError_t grow_workspace(LibWorkspace &w, size_t bytes) {
+    if (w.bytes >= bytes) return hipSuccess;
+    hipError_t err;
+    if (w.ptr != nullptr) {
+        if ((err = hipFreeAsync(w.ptr, w.stream)) != hipSuccess) return err;
         w.ptr = nullptr;
         w.bytes = 0;
-        const size_t grown = (bytes + (1u << 20) - 1) & ~static_cast<size_t>((1u << 20) - 1);
-        if ((err = hipMalloc(&w.ptr, grown)) != hipSuccess) return err;
-        w.bytes = grown;
-        *out = w.ptr;
-        return hipSuccess;
     }
     const size_t grown = (bytes + (1u << 20) - 1) & ~static_cast<size_t>((1u << 20) - 1);
-    void *p = nullptr;
-    if ((err = hipMalloc(&p, grown)) != hipSuccess) return err;
-    g_ws.push_back(LibWorkspace{dev, stream, p, grown});
-    *out = p;
+    if ((err = hipMallocAsync(&w.ptr, grown, w.stream)) != hipSuccess) {
+        w.ptr = nullptr;
+        return err;
+    }
+    w.bytes = grown;
     return hipSuccess;
 }
 
@@ -157,7 +184,9 @@ tra_status check_args(int variant, int64_t M, int64_t N, int64_t K, const float 
     }
     rung = resolve(variant, M, N, K);
     plan = plan_rung(rung, M, N, K);
-    if (plan.grid <= 0 || plan.grid > tra::kMaxGrid) return TRA_ERR_UNSUPPORTED;
+    if (plan.grid <= 0 || plan.grid > tra::kMaxGrid ||
+        plan.grid * plan.block > tra::kMaxGridLanes)
+        return TRA_ERR_UNSUPPORTED;
     return TRA_OK;
 }
 
@@ -179,11 +208,18 @@ tra_status gemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K, const 
     const tra::GemmArgs a{M, N, K, A, lda, B, ldb, C, ldc, static_cast<hipStream_t>(stream)};
     const size_t need = plan.workspace_bytes;
     if (need == 0) return hip_status(launch(v, a, nullptr, 0));
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    void *ws = nullptr;
-    const hipError_t err = library_workspace(a.stream, need, &ws);
+    // A buffer allocated in stream order while the stream is being captured
+    // would belong to the graph, not to the library: capture takes the
+    // caller's workspace (gemm_f32_variant_ws) instead.
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    hipError_t err = hipStreamIsCapturing(a.stream, &capture);
     if (err != hipSuccess) return hip_status(err);
-    return hip_status(launch(v, a, ws, need));
+    if (capture != hipStreamCaptureStatusNone) return TRA_ERR_UNSUPPORTED;
+    LibWorkspace *w = nullptr;
+    if ((err = find_workspace(a.stream, &w)) != hipSuccess) return hip_status(err);
+    std::lock_guard<std::mutex> lock(w->mutex);
+    if ((err = grow_workspace(*w, need)) != hipSuccess) return hip_status(err);
+    return hip_status(launch(v, a, w->ptr, w->bytes));
 }
 
 tra_status gemm_f32_variant_ws(int variant, int64_t M, int64_t N, int64_t K, const float *A,
@@ -225,10 +261,10 @@ tra_status tra_gemm_describe(int variant, int64_t M, int64_t N, int64_t K, char 
     const tra::LaunchPlan p = plan_rung(rung, M, N, K);
     std::snprintf(buf, len,
                   "variant=%s rung=%s kernel=%s tile=%dx%dx%d grid=%lld block=%d lds_bytes=%d "
-                  "split_k=%d stream_k_tiles=%lld stream_k_wgs=%lld split=%s workspace_bytes=%zu",
+                  "stream_k_tiles=%lld stream_k_wgs=%lld split=%s workspace_bytes=%zu",
                   tra_gemm_variant_name(variant),
                   tra_gemm_variant_name(rung), p.kernel, p.bm, p.bn, p.bk,
-                  static_cast<long long>(p.grid), p.block, p.lds_bytes, p.split_k,
+                  static_cast<long long>(p.grid), p.block, p.lds_bytes,
                   static_cast<long long>(p.sk_tiles), static_cast<long long>(p.sk_wgs),
                   p.split != nullptr ? p.split : "none", p.workspace_bytes);
     return TRA_OK;
@@ -257,5 +293,33 @@ const char *tra_gemm_variant_name(int variant) {
 }
 
 int tra_last_hip_error(void) { return g_last_hip_error; }
+
+tra_status tra_gemm_release_workspaces(void) {
+    std::lock_guard<std::mutex> list_lock(g_ws_list_mutex);
+    int current = -1;
+    hipError_t first = hipSuccess;
+    for (const auto &w : g_ws) {
+        std::lock_guard<std::mutex> lock(w->mutex);
+        if (w->ptr == nullptr) continue;
+        if (current < 0 && (first = hipGetDevice(&current)) != hipSuccess) break;
+        // the stream may be gone: wait for the whole device, then release
+        // the buffer on the null stream
+        hipError_t err = hipSetDevice(w->device);
+        if (err == hipSuccess) err = hipDeviceSynchronize();
+        if (err == hipSuccess) err = hipFreeAsync(w->ptr, nullptr);
+        if (err == hipSuccess) err = hipStreamSynchronize(nullptr);
+        if (err == hipSuccess) {
+            w->ptr = nullptr;
+            w->bytes = 0;
+        } else if (first == hipSuccess) {
+            first = err;
+        }
+    }
+    if (current >= 0) {
+        const hipError_t back = hipSetDevice(current);
+        if (first == hipSuccess) first = back;
+    }
+    return hip_status(first);
+}
 
 }  // extern "C"
