@@ -182,6 +182,32 @@ TRA_API tra_status gemm_f32_variant_ws(int variant,
                                void *stream);
 
 /*
+ * gemm_f32_variant_noalloc: as gemm_f32_variant, for callers that cannot
+ * allocate device memory -- code under stream capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It allocates nothing, on the
+ * host or the device: the stream-K split's partial tiles go to a scratch
+ * array of TRA_STATIC_SCRATCH_BYTES that is part of the library's code
+ * object (one per device, held until the process ends).  A call whose
+ * split needs more than that (tra_gemm_workspace_size) is refused with
+ * TRA_ERR_UNSUPPORTED before anything is enqueued; such callers pass their
+ * own buffer to gemm_f32_variant_ws instead.  Every call on a device
+ * shares that device's one array, and a call leaves its partial tiles
+ * there: calls that may overlap in time on one device (on different
+ * streams, or from threads without ordering) race and must be ordered by
+ * the caller, e.g. issued on one stream.  Nothing in the array needs to
+ * start at zero.  Otherwise the same arguments, results and status codes
+ * as gemm_f32_variant.
+ */
+#define TRA_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+
+TRA_API tra_status gemm_f32_variant_noalloc(int variant,
+                                    int64_t M, int64_t N, int64_t K,
+                                    const float *A, int64_t lda,
+                                    const float *B, int64_t ldb,
+                                    float *C, int64_t ldc,
+                                    void *stream);
+
+/*
  * tra_gemm_workspace_size: device scratch in bytes that gemm_f32_variant_ws
  * needs for this variant and these sizes on the current device (0 for every
  * variant except a stream-K split), written to *bytes.  Returns

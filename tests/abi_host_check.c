@@ -72,6 +72,10 @@ int main(void) {
     /* 2^24 workgroups of 256 lanes: 2^32 lanes, past HIP's limit */
     CHECK(gemm_f32_variant(TRA_GEMM_NAIVE, (int64_t)1 << 26, 64, 0, NULL, 0, NULL, 64, C, 64,
                            NULL) == TRA_ERR_UNSUPPORTED);
+    /* the no-alloc entry point: a split past its static scratch is refused */
+    CHECK(gemm_f32_variant_noalloc(TRA_GEMM_MFMA_STREAMK, 4608, 4608, 4096, A, 4096, B, 4608, C,
+                                   4608, NULL) == TRA_ERR_UNSUPPORTED);
+    CHECK(gemm_f32_variant_noalloc(42, 4, 4, 4, A, 4, B, 4, C, 4, NULL) == TRA_ERR_INVALID_ARG);
     /* nothing to compute: OK, no launch */
     CHECK(gemm_f32(0, 4, 4, NULL, 4, NULL, 4, NULL, 4, NULL) == TRA_OK);
     /* no workspace was allocated: nothing to release */

@@ -162,6 +162,25 @@ def test_lane_count_past_32_bits_is_unsupported():
     assert st == tra.TRA_ERR_UNSUPPORTED
 
 
+def test_noalloc_refuses_splits_past_its_scratch():
+    # the stream-K runs of 4608^2 x 4096 need two 256 x 128 partial tiles for
+    # each of 256 workgroups, 64 MiB, past the 32 MiB static scratch: refused
+    # on the host, before anything is enqueued (nothing here touches a GPU)
+    need = tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, 4608, 4608, 4096)
+    assert need == 64 << 20 > tra.STATIC_SCRATCH_BYTES
+    st = tra.gemm_f32_variant_noalloc(tra.MFMA_STREAMK, 4608, 4608, 4096, A_ADDR, 4096, B_ADDR,
+                                      4608, C_ADDR, 4608, None)
+    assert st == tra.TRA_ERR_UNSUPPORTED
+    # argument checks come first, as in gemm_f32_variant
+    assert tra.gemm_f32_variant_noalloc(tra.MFMA, 4, 4, 4, None, 4, B_ADDR, 4, C_ADDR, 4,
+                                        None) == tra.TRA_ERR_INVALID_ARG
+    assert tra.gemm_f32_variant_noalloc(tra.MFMA, 0, 4, 4, None, 4, None, 4, None, 4,
+                                        None) == tra.TRA_OK
+    # the header's constant and the binding's agree
+    text = open(HEADER).read()
+    assert "#define TRA_STATIC_SCRATCH_BYTES ((size_t)32 << 20)" in text
+
+
 def test_release_without_workspaces_touches_nothing():
     # nothing was allocated in this process: OK without any HIP call
     assert tra.tra_gemm_release_workspaces() == tra.TRA_OK

@@ -11,6 +11,8 @@ Low-level calls take raw device addresses (ints) and a hipStream_t handle:
     gemm_f32_variant(variant, M, N, K, A, lda, B, ldb, C, ldc, stream) -> status
     gemm_f32_variant_ws(variant, M, N, K, A, lda, B, ldb, C, ldc,
                         workspace, workspace_bytes, stream) -> status
+    gemm_f32_variant_noalloc(variant, M, N, K, A, lda, B, ldb, C, ldc,
+                             stream) -> status
 
 ``matmul(A, B, C=None, variant=AUTO)`` is the torch-tensor convenience
 form: it checks the tensors, passes their device pointers and torch's
@@ -43,6 +45,7 @@ VARIANTS = {"auto": AUTO, "naive": NAIVE, "lds_tiled": LDS_TILED,
 LADDER = (NAIVE, LDS_TILED, REGBLOCK_DB, MFMA)
 
 ABI_FUNCTIONS = ("gemm_f32", "gemm_f32_variant", "gemm_f32_variant_ws",
+                 "gemm_f32_variant_noalloc",
                  "tra_gemm_workspace_size", "tra_gemm_release_workspaces",
                  "tra_gemm_describe", "tra_status_string",
                  "tra_gemm_variant_name", "tra_last_hip_error", "tra_probe_work",
@@ -54,6 +57,9 @@ PROBE_MFMA = 1
 PROBE_FMA = 2
 PROBE_BLOCKS = 1024
 PROBE_SINK_FLOATS = PROBE_BLOCKS * 256
+
+# TRA_STATIC_SCRATCH_BYTES: the scratch of gemm_f32_variant_noalloc
+STATIC_SCRATCH_BYTES = 32 << 20
 
 
 class TraError(RuntimeError):
@@ -106,6 +112,8 @@ def _open(path: str) -> ctypes.CDLL:
     lib.gemm_f32_variant_ws.argtypes = [c_int, i64, i64, i64, p, i64, p, i64, p, i64, p,
                                         ctypes.c_size_t, p]
     lib.gemm_f32_variant_ws.restype = c_int
+    lib.gemm_f32_variant_noalloc.argtypes = [c_int, i64, i64, i64, p, i64, p, i64, p, i64, p]
+    lib.gemm_f32_variant_noalloc.restype = c_int
     lib.tra_gemm_workspace_size.argtypes = [c_int, i64, i64, i64,
                                             ctypes.POINTER(ctypes.c_size_t)]
     lib.tra_gemm_workspace_size.restype = c_int
@@ -144,6 +152,10 @@ def gemm_f32_variant_ws(variant, M, N, K, A, lda, B, ldb, C, ldc, workspace, wor
                         stream=None) -> int:
     return load().gemm_f32_variant_ws(variant, M, N, K, A, lda, B, ldb, C, ldc, workspace,
                                       workspace_bytes, stream)
+
+
+def gemm_f32_variant_noalloc(variant, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return load().gemm_f32_variant_noalloc(variant, M, N, K, A, lda, B, ldb, C, ldc, stream)
 
 
 def tra_gemm_workspace_size(variant: int, M: int, N: int, K: int) -> int:

@@ -140,6 +140,36 @@ hipError_t grow_workspace(LibWorkspace &w, size_t bytes) {
     return hipSuccess;
 }
 
+// Scratch of gemm_f32_variant_noalloc: one array per device, part of the
+// library's code object, so that entry point never allocates.  The host
+// name `scratch` is only a stand-in for the device array: its device
+// address is looked up once per device (hipGetSymbolAddress, on the
+// entry point's first call there, with that device current) and that
+// address is what the kernels get.  Every call on a device shares the one
+// array; nothing in it has to start at zero (each split writes every
+// partial tile it later reads).
+constexpr size_t kStaticScratchBytes = size_t{32} << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current device's scratch array.
+hipError_t static_scratch(void **out) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        if ((err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess) return err;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 hipError_t launch(int variant, const tra::GemmArgs &a, void *ws, size_t ws_bytes) {
     switch (variant) {
         case TRA_GEMM_NAIVE: return tra::launch_naive(a);
@@ -237,6 +267,25 @@ tra_status gemm_f32_variant_ws(int variant, int64_t M, int64_t N, int64_t K, con
         return TRA_ERR_INVALID_ARG;
     const tra::GemmArgs a{M, N, K, A, lda, B, ldb, C, ldc, static_cast<hipStream_t>(stream)};
     return hip_status(launch(v, a, workspace, workspace_bytes));
+}
+
+tra_status gemm_f32_variant_noalloc(int variant, int64_t M, int64_t N, int64_t K,
+                                    const float *A, int64_t lda, const float *B, int64_t ldb,
+                                    float *C, int64_t ldc, void *stream) {
+    bool noop = false;
+    int v = 0;
+    tra::LaunchPlan plan{};
+    const tra_status st = check_args(variant, M, N, K, A, lda, B, ldb, C, ldc, noop, v, plan);
+    if (st != TRA_OK || noop) return st;
+    const size_t need = plan.workspace_bytes;
+    if (need > kStaticScratchBytes) return TRA_ERR_UNSUPPORTED;
+    void *ws = nullptr;
+    if (need > 0) {
+        const hipError_t err = static_scratch(&ws);
+        if (err != hipSuccess) return hip_status(err);
+    }
+    const tra::GemmArgs a{M, N, K, A, lda, B, ldb, C, ldc, static_cast<hipStream_t>(stream)};
+    return hip_status(launch(v, a, ws, need > 0 ? kStaticScratchBytes : 0));
 }
 
 tra_status tra_gemm_workspace_size(int variant, int64_t M, int64_t N, int64_t K,
