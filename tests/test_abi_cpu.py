@@ -75,7 +75,8 @@ def test_describe_plans():
     d = tra.tra_gemm_describe(tra.NAIVE, 1024, 1024, 1024)
     assert "gemm_naive_f32" in d and "grid=4096" in d and "block=256" in d
     d = tra.tra_gemm_describe(tra.LDS_TILED, 1024, 1024, 1024)
-    assert "tile=32x32x32" in d and "block=1024" in d
+    assert "tile=16x16x64" in d and "block=256" in d and "grid=4096" in d
+    assert "lds_bytes=8704" in d
     d = tra.tra_gemm_describe(tra.REGBLOCK_DB, 3000, 2049, 1531)
     assert "grid=1551" in d and "64x64" in d    # 408 tiles of 128 x 128 are too few
     d = tra.tra_gemm_describe(tra.REGBLOCK_DB, 4096, 4096, 4096)
