@@ -73,17 +73,40 @@ bool prefer_stream_k(int64_t M, int64_t N, int64_t K);
 // XCD has its own L2.  The remap gives each XCD a contiguous run of logical
 // tile ids so that the tiles it runs at the same time share rows of A and
 // columns of B in its L2.  A bijection on [0, n) for any n.
-__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t n) {
+__host__ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t n) {
     constexpr int64_t kXcds = 8;
     const int64_t q = n / kXcds, r = n % kXcds;
     const int64_t x = bid % kXcds, slot = bid / kXcds;
     return x * q + (x < r ? x : r) + slot;
 }
 
+// The same two maps in 32-bit arithmetic, cheaper than the 64-bit
+// divisions at the start of every workgroup.  Safe for any launch the host
+// accepts: at most 2^32 - 1 lanes, so at most 2^24 workgroups of 256 lanes
+// (2^23 of 512), and G * tiles_n stays far below 2^31.
+__host__ __device__ __forceinline__ int xcd_remap32(int bid, int n) {
+    const int q = n >> 3, r = n & 7;
+    const int x = bid & 7, slot = bid >> 3;
+    return x * q + (x < r ? x : r) + slot;
+}
+
+template <int G>
+__host__ __device__ __forceinline__ void grouped_tile32(int id, int tiles_m, int tiles_n, int &tm,
+                                                       int &tn) {
+    const unsigned per_group = static_cast<unsigned>(G) * static_cast<unsigned>(tiles_n);
+    const unsigned g = static_cast<unsigned>(id) / per_group;
+    const int first = static_cast<int>(g) * G;
+    const int rows = (tiles_m - first) < G ? (tiles_m - first) : G;
+    const unsigned in = static_cast<unsigned>(id) - g * per_group;
+    const unsigned q = in / static_cast<unsigned>(rows);
+    tm = first + static_cast<int>(in - q * static_cast<unsigned>(rows));
+    tn = static_cast<int>(q);
+}
+
 // Logical tile id -> (tile row, tile column) in groups of `group` tile rows
 // swept column by column, so that consecutive ids reuse the same B columns
 // and a small set of A rows.
-__device__ __forceinline__ void grouped_tile(int64_t id, int64_t tiles_m, int64_t tiles_n,
+__host__ __device__ __forceinline__ void grouped_tile(int64_t id, int64_t tiles_m, int64_t tiles_n,
                                              int64_t group, int64_t &tm, int64_t &tn) {
     const int64_t per_group = group * tiles_n;
     const int64_t g = id / per_group;

@@ -26,8 +26,9 @@
 //
 // LDS layout (two buffers):
 //   As[m][k]  k contiguous, row stride BK + 4 words: a global float4 along k
-//             stores as one ds_write_b128, and 8 consecutive rows read by
-//             ds_read_b128 fall in disjoint bank groups.
+//             stores as one ds_write_b128, and 16 consecutive rows read (or
+//             stored) at one k quad fall in disjoint bank groups; staging
+//             gives each group of 16 lanes one quad of 16 rows (a_quad_of).
 //   Bs[k][n]  n contiguous, row stride BN + 4 words.
 //
 // Pipeline (slice s lives in LDS buffer s % 2; NR register sets hold the
@@ -94,6 +95,11 @@ struct MfmaTile {
     static constexpr int B_F4 = (B_VEC + THREADS - 1) / THREADS;
     static constexpr int LDS_WORDS = 2 * (BM * AST + BK * BST);
     static constexpr int UNROLL = NR == 4 ? 4 : 2;
+    // Tile rows per group of the tile order (grouped_tile).  One XCD runs 32
+    // workgroups at once, one a CU; 4 rows of 256 x 128 tiles make that a
+    // 1024 x 1024 block of C (A and B slices of equal size), where 8 rows
+    // made it 2048 x 512 (25% more operand bytes per slice from memory).
+    static constexpr int GROUP = BM == 256 ? 4 : 8;
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be 32x32 blocks");
     static_assert(BM % WM == 0 && BN % WN == 0, "block tile must be whole wave tiles");
     static_assert(HALF % 4 == 0, "each lane half needs a multiple of 4 k per slice");
@@ -112,6 +118,20 @@ struct Ctx {
     int t;
 };
 
+// The row m and k quad kq of A that staging lane-slot f moves: 16
+// consecutive slots take the same quad of 16 consecutive rows.  Their LDS
+// stores then start (BK + 4) = 20 words apart, in distinct 4-bank groups,
+// like the fragment reads; with 4 consecutive slots per row (4 quads of one
+// row, then the next row) each 16-slot group of stores spanned rows that
+// share banks (one conflict cycle per LDS instruction).  A wave still reads
+// 16 whole 64-byte row segments per load.
+template <class T>
+__device__ __forceinline__ void a_quad_of(int f, int &m, int &kq) {
+    static_assert(T::BK == 16 && T::BM % 16 == 0, "4 quads per row, rows in groups of 16");
+    m = (f >> 6) * 16 + (f & 15);
+    kq = (f >> 4) & 3;
+}
+
 // Loads slice k0 .. k0+BK of the A and B tiles into registers.
 template <class T, int MODE>
 __device__ __forceinline__ void fetch(const Ctx<T> &c, int64_t k0, float4 (&ra)[T::A_F4],
@@ -120,7 +140,8 @@ __device__ __forceinline__ void fetch(const Ctx<T> &c, int64_t k0, float4 (&ra)[
     for (int r = 0; r < T::A_F4; ++r) {
         const int f = c.t + T::THREADS * r;
         if (T::A_VEC % T::THREADS != 0 && f >= T::A_VEC) break;
-        const int m = f / (T::BK / 4), kq = f % (T::BK / 4);
+        int m, kq;
+        a_quad_of<T>(f, m, kq);
         const float *p = c.A + (c.m0 + m) * c.lda + k0 + 4 * kq;
         if (MODE == kVec || MODE == kVecA) ra[r] = *reinterpret_cast<const float4 *>(p);
         else if (MODE == kScalar) ra[r] = load4_scalar(p);
@@ -156,7 +177,8 @@ __device__ __forceinline__ void stage(float *lds, int buf, int t, const float4 (
     for (int r = 0; r < T::A_F4; ++r) {
         const int f = t + T::THREADS * r;
         if (T::A_VEC % T::THREADS != 0 && f >= T::A_VEC) break;
-        const int m = f / (T::BK / 4), kq = f % (T::BK / 4);
+        int m, kq;
+        a_quad_of<T>(f, m, kq);
         *reinterpret_cast<float4 *>(&as[m * T::AST + 4 * kq]) = ra[r];
     }
 #pragma unroll
@@ -530,7 +552,7 @@ __device__ __forceinline__ void sk_fixup(int job, int64_t M, int64_t N, float *C
     const int w_hi = sk_owner(p, (tile + 1) * ipt - 1);
     if (w_lo == w_hi) return;
     int64_t tm, tn;
-    grouped_tile(tile, p.tiles_m, p.tiles_n, 8, tm, tn);
+    grouped_tile(tile, p.tiles_m, p.tiles_n, T::GROUP, tm, tn);
     const Origin o = tile_origin<BM, BN>(tm, tn, M, N);
     const int row = f / (BN / 4), col = 4 * (f % (BN / 4));
     const int64_t gm = o.m0 + row, gn = o.n0 + col;
@@ -569,7 +591,7 @@ __device__ __forceinline__ void part_fixup(int job, int64_t M, int64_t N, float 
     const int tile = job / fix_chunks<T>();
     const int f = (job % fix_chunks<T>()) * T::THREADS + static_cast<int>(threadIdx.x);
     int64_t tm, tn;
-    grouped_tile(tile, p.tiles_m, p.tiles_n, 8, tm, tn);
+    grouped_tile(tile, p.tiles_m, p.tiles_n, T::GROUP, tm, tn);
     const Origin o = tile_origin<BM, BN>(tm, tn, M, N);
     const int row = f / (BN / 4), col = 4 * (f % (BN / 4));
     const int64_t gm = o.m0 + row, gn = o.n0 + col;
@@ -610,9 +632,9 @@ void gemm_mfma_f32(int64_t M, int64_t N, int64_t K,
         return;
     }
     const int dp = p.tiles_m * p.tiles_n - p.sk_tiles;
-    const int tile = p.sk_tiles + static_cast<int>(xcd_remap(bid - fix, dp));
-    int64_t tm, tn;
-    grouped_tile(tile, p.tiles_m, p.tiles_n, 8, tm, tn);
+    const int tile = p.sk_tiles + xcd_remap32(bid - fix, dp);
+    int tm, tn;
+    grouped_tile32<T::GROUP>(tile, p.tiles_m, p.tiles_n, tm, tn);
     const Origin o = tile_origin<T::BM, T::BN>(tm, tn, M, N);
     const Ctx<T> c{M, N, K, A, lda, B, ldb, o.m0, o.n0, static_cast<int>(threadIdx.x)};
     const int64_t rows = M - o.m0 < T::BM ? M - o.m0 : T::BM;
@@ -644,7 +666,7 @@ void gemm_mfma_f32_sk(int64_t M, int64_t N, int64_t K,
         const int tile = it / ipt, kb = it - tile * ipt;
         const int ke = ipt < kb + (end - it) ? ipt : kb + (end - it);
         int64_t tm, tn;
-        grouped_tile(tile, p.tiles_m, p.tiles_n, 8, tm, tn);
+        grouped_tile(tile, p.tiles_m, p.tiles_n, T::GROUP, tm, tn);
         const Origin o = tile_origin<T::BM, T::BN>(tm, tn, M, N);
         c.m0 = o.m0;
         c.n0 = o.n0;
@@ -709,7 +731,7 @@ void gemm_mfma_f32_parts(int64_t M, int64_t N, int64_t K,
         tile = p.sk_tiles + static_cast<int>(xcd_remap(bid - split, dp));
     }
     int64_t tm, tn;
-    grouped_tile(tile, p.tiles_m, p.tiles_n, 8, tm, tn);
+    grouped_tile(tile, p.tiles_m, p.tiles_n, T::GROUP, tm, tn);
     const Origin o = tile_origin<T::BM, T::BN>(tm, tn, M, N);
     const Ctx<T> c{M, N, K, A, lda, B, ldb, o.m0, o.n0, static_cast<int>(threadIdx.x)};
     if (part >= 0) {                       // a part: the whole block tile to its slot
