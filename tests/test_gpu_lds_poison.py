@@ -38,6 +38,9 @@ SHAPES = [
     (40, 2000, 700),      # shorter than a tile: float4 loads, rows past M zeroed
     (3000, 33, 1100),     # narrower than a tile, N odd: element loads
     (200, 66000, 40),     # 256 x 128 tiles taller than M
+    (1000, 1000, 1007),   # register-blocked rung: K split over 3 lane groups, K tail
+    (300, 700, 255),      # register-blocked rung: K split over 4 lane groups
+    (100, 200, 127),      # register-blocked rung: K split over 2 lane groups
 ]
 
 

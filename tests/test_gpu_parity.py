@@ -7,10 +7,11 @@ Acceptance:
     summation gives the same value; compared with ==, so +0 and -0 are equal);
   * floating-point inputs: |C_gpu - C64| <= 1e-5 * S per element, where C64
     is the oracle's binary64 sum and S = sum_k |A_ik * B_kj|.
-Full-size shapes are checked on sampled entries the oracle computes one by
-one (whole rows and columns at tile edges plus random entries); the
-integer patterns are checked on every element through their period
-(C depends only on i mod 13 and j mod 7).
+Full-size shapes are checked on every element against the oracle's full
+product, and on sampled entries the oracle computes one by one (whole rows
+and columns at tile edges plus random entries); the integer patterns are
+checked on every element through their period (C depends only on i mod 13
+and j mod 7).
 """
 from __future__ import annotations
 
@@ -168,17 +169,22 @@ LARGE = ["normal4096", "ragged", "tall", "rowslab4096", "kslab_tall"]
 
 
 @pytest.mark.parametrize("name", LARGE)
-@pytest.mark.parametrize("variant", RUNGS, ids=RUNG_IDS)
-def test_large_configs_sampled(variant, name):
+@pytest.mark.parametrize("variant", RUNGS + [tra.AUTO], ids=RUNG_IDS + ["auto"])
+def test_large_configs_every_element(variant, name):
+    # every element against the oracle's full product (computed once per
+    # configuration: about 20 s at 4096^3 on 16 cores), and a sample of
+    # rows, columns and random entries computed directly, one by one
     w = inputs.WORKLOADS[name]
     log(f"[case] {tra.tra_gemm_variant_name(variant)} {name} {w.M}x{w.N}x{w.K} "
         f"({tra.tra_gemm_describe(variant, w.M, w.N, w.K)})")
     A, B = workload_inputs(name)
     C, *_ = run_gpu(variant, A, B)
+    ref = oracle_full(name)
+    ratio = assert_tol(C, ref.c64, ref.s64, name)
+    log(f"[case]   every element within 1e-5 * S; max |diff|/S = {ratio:.2e}")
     rows, cols = sample_entries(w.M, w.N, seed=w.M)
-    ref = oracle.gemm_entries(A, B, rows, cols)
-    assert_tol(C[rows, cols], ref.c64, ref.s64, name)
-    assert np.isfinite(C).all()
+    direct = oracle.gemm_entries(A, B, rows, cols)
+    assert_tol(C[rows, cols], direct.c64, direct.s64, f"{name} (direct)")
 
 
 @pytest.mark.parametrize("name", LARGE)
@@ -277,6 +283,40 @@ def test_tile_shapes_with_tails(variant, shape):
     A, B, ref = tile_shape_case(M, N, K)
     C, *_ = run_gpu(variant, A, B)
     assert_tol(C, ref.c64, ref.s64, f"{M}x{N}x{K}")
+
+
+# Shapes that send the register-blocked rung to its K split inside the
+# workgroup (4, 3 or 2 lane groups each running an equal share of the K
+# slices), with tails on every axis: (M, N, K, lane groups).
+REGBLOCK_SPLIT_SHAPES = [
+    (1024, 1024, 1024, 4),   # the 1024^3 configuration: 256 tiles, 64 slices
+    (1000, 1000, 1000, 3),   # 63 slices, the last one partial; edge tiles moved inside
+    (1000, 1000, 1007, 3),   # K tail 15 of 16
+    (300, 700, 255, 4),      # 16 slices, the last partial
+    (100, 200, 127, 2),      # 8 slices
+    (60, 50, 760, 4),        # one tile larger than the matrix (checked loads)
+    (2048, 512, 1024, 4),    # 256 tiles, 2048 x 512
+]
+
+
+@pytest.mark.parametrize("shape", REGBLOCK_SPLIT_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}x{s[2]}")
+def test_regblock_k_split(shape):
+    M, N, K, groups = shape
+    d = tra.tra_gemm_describe(tra.REGBLOCK_DB, M, N, K)
+    log(f"[case] regblock K split {M}x{N}x{K} ({d})")
+    assert f"K in {groups}>" in d
+    A, B = inputs.uniform(M, K, 91), inputs.uniform(K, N, 92)
+    ref = oracle.gemm(A, B)
+    C, *_ = run_gpu(tra.REGBLOCK_DB, A, B)
+    assert_tol(C, ref.c64, ref.s64, f"{M}x{N}x{K}")
+    Ai, Bi = inputs.small_ints(M, K, M + 3), inputs.small_ints(K, N, N + 5)
+    Ci, *_ = run_gpu(tra.REGBLOCK_DB, Ai, Bi)
+    assert_exact(Ci, oracle.gemm(Ai, Bi).c32, f"small ints {M}x{N}x{K}")
+    # odd strides and 4-byte offsets: element loads, element stores
+    Cs, buf, ldc_, off = run_gpu(tra.REGBLOCK_DB, Ai, Bi, K + 3, N + 5, N + 7, (1, 3, 1))
+    assert_exact(Cs, oracle.gemm(Ai, Bi).c32, f"odd strides {M}x{N}x{K}")
+    full = buf[off:off + M * ldc_].reshape(M, ldc_)
+    assert np.all(full[:, N:] == C_SENTINEL)
 
 
 @functools.lru_cache(maxsize=None)

@@ -28,7 +28,8 @@
 //   As[m][k]  k contiguous, row stride BK + 4 words: a global float4 along k
 //             stores as one ds_write_b128, and 16 consecutive rows read (or
 //             stored) at one k quad fall in disjoint bank groups; staging
-//             gives each group of 16 lanes one quad of 16 rows (a_quad_of).
+//             spreads each group of 16 lanes' stores over all 64 banks
+//             (a_quad_of).
 //   Bs[k][n]  n contiguous, row stride BN + 4 words.
 //
 // Pipeline (slice s lives in LDS buffer s % 2; NR register sets hold the
@@ -118,18 +119,22 @@ struct Ctx {
     int t;
 };
 
-// The row m and k quad kq of A that staging lane-slot f moves: 16
-// consecutive slots take the same quad of 16 consecutive rows.  Their LDS
-// stores then start (BK + 4) = 20 words apart, in distinct 4-bank groups,
-// like the fragment reads; with 4 consecutive slots per row (4 quads of one
-// row, then the next row) each 16-slot group of stores spanned rows that
-// share banks (one conflict cycle per LDS instruction).  A wave still reads
-// 16 whole 64-byte row segments per load.
+// The row m and k quad kq of A that staging lane-slot f moves.  Four
+// consecutive slots take the four quads of one row (a contiguous 64-byte
+// segment of A, one request); the 16 slots that store together take rows
+// a, a+4, a+8 and a+12 of a 16-row group.  With rows BK + 4 = 20 words
+// apart, row m starts at 4-bank group 5m mod 16, so those rows start at
+// groups 5a, 5a+4, 5a+8 and 5a+12: four disjoint runs of four groups, all
+// 64 banks once.  (Four consecutive rows instead put rows a and a+3 in the
+// same banks: one conflict cycle per LDS instruction.  Giving 16
+// consecutive slots one quad of 16 rows removed the conflicts too, but cost
+// 2% at 1024^3 with cold caches: neighbouring lanes then read different
+// rows.)
 template <class T>
 __device__ __forceinline__ void a_quad_of(int f, int &m, int &kq) {
     static_assert(T::BK == 16 && T::BM % 16 == 0, "4 quads per row, rows in groups of 16");
-    m = (f >> 6) * 16 + (f & 15);
-    kq = (f >> 4) & 3;
+    m = (f >> 6) * 16 + ((f >> 4) & 3) + 4 * ((f >> 2) & 3);
+    kq = f & 3;
 }
 
 // Loads slice k0 .. k0+BK of the A and B tiles into registers.

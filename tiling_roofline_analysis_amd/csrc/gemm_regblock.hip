@@ -20,7 +20,12 @@
 //   * a tile at the bottom or right edge is moved back inside the matrix
 //     (tile_origin), so full slices load with no bounds checks; only the
 //     slice that runs past K, and matrices smaller than a tile, load with
-//     checks.
+//     checks;
+//   * with no more 64 x 64 tiles than CUs (1024^3), one 256-lane workgroup
+//     per tile would leave one wave per SIMD to hide the latencies of a
+//     VALU loop; there the tile's workgroup has 2-4 lane groups, each
+//     running an equal share of the K slices in LDS buffers of its own, and
+//     their partial tiles are added in a fixed order at the end.
 //
 // gfx950 layout (256 lanes = 4 wave64s, lane t: tx = t % 16, ty = t / 16),
 // for the 128 x 128 tile (the 64 x 64 one keeps i < 4 and the first group):
@@ -148,25 +153,32 @@ __device__ __forceinline__ void rb_compute(const float *as, const float *bs, int
     }
 }
 
-// The K loop of one tile.  Slices that lie wholly inside K load in MODE
-// with no checks and no branch in the loop; the slice that runs past K (if
-// any) loads with checks.
-template <class T, int MODE>
+// The K loop of one tile: all of K, or with RANGE the slices s0 .. s0+n-1
+// (n >= 1; at most the last of them runs past K).  Slices that lie wholly
+// inside K load in MODE with no checks and no branch in the loop; the slice
+// that runs past K (if any) loads with checks.  A call makes one workgroup
+// barrier per slice.  (Without RANGE the first slice is 0 at compile time:
+// a run-time start made the compiler's code for the whole-K loop up to 55%
+// slower, at 1000^3.)
+template <class T, int MODE, bool RANGE = false>
 __device__ __forceinline__ void rb_k_loop(const RbCtx &c, float *As, float *Bs, int tx, int ty,
-                                          float (&acc)[T::TM][T::TN]) {
+                                          float (&acc)[T::TM][T::TN], int64_t first = 0,
+                                          int64_t count = 0) {
     constexpr int BK = T::BK;
     constexpr int AW = T::BM * T::AST, BW = BK * T::BST;   // words per LDS buffer
-    const int64_t slices = ceil_div(c.K, BK), full = c.K / BK;
-    if (slices == 0) return;
+    const int64_t s0 = RANGE ? first : 0;
+    const int64_t slices = RANGE ? count : ceil_div(c.K, BK);
+    const int64_t full = RANGE ? (c.K / BK - s0 < count ? c.K / BK - s0 : count) : c.K / BK;
+    if (slices <= 0) return;
     float4 ra[T::AF4], rb[T::BF4];
-    if (full > 0) rb_fetch<T, MODE>(c, 0, ra, rb);
-    else rb_fetch<T, kChecked>(c, 0, ra, rb);
+    if (full > 0) rb_fetch<T, MODE>(c, s0 * BK, ra, rb);
+    else rb_fetch<T, kChecked>(c, s0 * BK, ra, rb);
     rb_stage<T>(As, Bs, c.t, ra, rb);
     __syncthreads();
     int64_t s = 0;
     for (; s + 1 < full; ++s) {
         const int cur = static_cast<int>(s & 1);
-        rb_fetch<T, MODE>(c, (s + 1) * BK, ra, rb);
+        rb_fetch<T, MODE>(c, (s0 + s + 1) * BK, ra, rb);
         rb_compute<T>(As + cur * AW, Bs + cur * BW, tx, ty, acc);
         rb_stage<T>(As + (cur ^ 1) * AW, Bs + (cur ^ 1) * BW, c.t, ra, rb);
         __syncthreads();
@@ -177,7 +189,7 @@ __device__ __forceinline__ void rb_k_loop(const RbCtx &c, float *As, float *Bs, 
     // tile's registers.)
     if (s + 1 < slices) {
         const int cur = static_cast<int>(s & 1);
-        rb_fetch<T, kChecked>(c, (s + 1) * BK, ra, rb);
+        rb_fetch<T, kChecked>(c, (s0 + s + 1) * BK, ra, rb);
         rb_compute<T>(As + cur * AW, Bs + cur * BW, tx, ty, acc);
         rb_stage<T>(As + (cur ^ 1) * AW, Bs + (cur ^ 1) * BW, c.t, ra, rb);
         __syncthreads();
@@ -185,6 +197,25 @@ __device__ __forceinline__ void rb_k_loop(const RbCtx &c, float *As, float *Bs, 
     }
     const int cur = static_cast<int>(s & 1);
     rb_compute<T>(As + cur * AW, Bs + cur * BW, tx, ty, acc);
+}
+
+// Stores rows and columns of the tile at o that it owns (a moved tile's
+// first skip_m rows and skip_n columns belong to the tile before it): the
+// float4 v = C[o.m0 + r][o.n0 + col .. col+3], as one store where all four
+// columns are owned, in range and aligned.
+__device__ __forceinline__ void rb_store4(float *C, int64_t ldc, int64_t M, int64_t N,
+                                          const Origin &o, int r, int col, float4 v, int vec_c) {
+    const int64_t gm = o.m0 + r, gn = o.n0 + col;
+    if (r < o.skip_m || gm >= M) return;
+    float *crow = C + gm * ldc;
+    if (vec_c && col >= o.skip_n && gn + 3 < N && (gn & 3) == 0) {
+        *reinterpret_cast<float4 *>(crow + gn) = v;
+    } else {
+        const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (col + j >= o.skip_n && gn + j < N) crow[gn + j] = e[j];
+    }
 }
 
 template <class T>
@@ -247,6 +278,83 @@ void gemm_regblock_f32(int64_t M, int64_t N, int64_t K,
     }
 }
 
+// The K axis split inside one workgroup of KS x 256 lanes: lane group g
+// runs the tile's slices [g n / KS, (g+1) n / KS) (n = KS x a whole number
+// of slices, so every group makes the same number of barriers) in LDS
+// buffers of its own, and the KS partial tiles are added in group order
+// through LDS at the end.  With fewer tiles than CUs, one 256-lane
+// workgroup per tile leaves each SIMD one wave to hide the LDS and memory
+// latency of a VALU loop; KS groups give it KS.
+template <class T, int KS>
+__global__ __launch_bounds__(T::THREADS * KS)
+void gemm_regblock_f32_ks(int64_t M, int64_t N, int64_t K,
+                          const float *__restrict__ A, int64_t lda,
+                          const float *__restrict__ B, int64_t ldb,
+                          float *__restrict__ C, int64_t ldc,
+                          int64_t tiles_m, int64_t tiles_n,
+                          int vec_a, int vec_b, int vec_c)
+{
+    constexpr int BM = T::BM, BN = T::BN, TM = T::TM, TN = T::TN;
+    constexpr int GW = 2 * BM * T::AST + 2 * T::BK * T::BST;   // LDS words per group
+    constexpr int PST = BN + 4;                                 // partial tile row stride
+    constexpr int WORDS = KS * GW > KS * BM * PST ? KS * GW : KS * BM * PST;
+    static_assert(TN == 4, "one float4 of C per micro-tile row");
+    __shared__ __attribute__((aligned(16))) float lds[WORDS];
+    lds_poison(lds, WORDS);
+
+    const int g = static_cast<int>(threadIdx.x) / T::THREADS;
+    const int t = static_cast<int>(threadIdx.x) % T::THREADS;
+    const int tx = t % 16, ty = t / 16;
+    int64_t tm, tn;
+    grouped_tile(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, 8, tm, tn);
+    const Origin o = tile_origin<BM, BN>(tm, tn, M, N);
+    const RbCtx c{M, N, K, A, lda, B, ldb, o.m0, o.n0, t};
+
+    float acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = 0.0f;
+
+    const int64_t per = ceil_div(K, T::BK) / KS;
+    float *As = lds + g * GW;
+    float *Bs = As + 2 * BM * T::AST;
+    const bool inside = o.m0 + BM <= M && o.n0 + BN <= N;
+    if (!inside)
+        rb_k_loop<T, kChecked, true>(c, As, Bs, tx, ty, acc, g * per, per);
+    else if (vec_a && vec_b && (o.n0 & 3) == 0)
+        rb_k_loop<T, kVec, true>(c, As, Bs, tx, ty, acc, g * per, per);
+    else if (vec_a)
+        rb_k_loop<T, kVecA, true>(c, As, Bs, tx, ty, acc, g * per, per);
+    else
+        rb_k_loop<T, kScalar, true>(c, As, Bs, tx, ty, acc, g * per, per);
+
+    // the partial tiles, row-major with rows of PST words, then each lane
+    // adds one float4 of the tile over the groups and stores it
+    __syncthreads();
+    float *part = lds + g * BM * PST;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+        *reinterpret_cast<float4 *>(&part[(ty + 16 * i) * PST + 4 * tx]) =
+            make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    __syncthreads();
+    constexpr int Q = BM * BN / 4;                       // float4 of C per tile
+#pragma unroll
+    for (int q = static_cast<int>(threadIdx.x); q < Q; q += T::THREADS * KS) {
+        const int r = q / (BN / 4), col = 4 * (q % (BN / 4));
+        float4 s = *reinterpret_cast<const float4 *>(&lds[r * PST + col]);
+#pragma unroll
+        for (int h = 1; h < KS; ++h) {
+            const float4 v = *reinterpret_cast<const float4 *>(&lds[(h * BM + r) * PST + col]);
+            s.x += v.x;
+            s.y += v.y;
+            s.z += v.z;
+            s.w += v.w;
+        }
+        rb_store4(C, ldc, M, N, o, r, col, s, vec_c);
+    }
+}
+
 // 128 x 128 tiles with 8 x 8 micro-tiles, or 64 x 64 tiles with 4 x 4.
 // The large tile runs best at two or more tiles per CU (three workgroups
 // fit on one); it is used when there are at least 2 x 256 of them and they
@@ -282,6 +390,19 @@ LaunchPlan plan_reg(int64_t M, int64_t N, const char *name) {
     return p;
 }
 
+// The in-workgroup K split, for at most one small tile per CU: the number
+// of lane groups, 4, 3 or 2 (the first that cuts K's slices into equal
+// runs of at least 4), or 0 for no split.  Measured on MI355X with four
+// groups: 1024^3 53.7 -> 32.7 us, 1024^2 x 4096 204 -> 120 us.
+int split_k_groups(int64_t M, int64_t N, int64_t K) {
+    const int64_t tiles = ceil_div(M, RegSmall::BM) * ceil_div(N, RegSmall::BN);
+    const int64_t slices = ceil_div(K, RegSmall::BK);
+    if (!small_tiles(M, N) || tiles > kCUs) return 0;
+    for (int ks : {4, 3, 2})
+        if (slices % ks == 0 && slices >= 4 * ks) return ks;
+    return 0;
+}
+
 template <class T>
 hipError_t launch_reg(const GemmArgs &a) {
     const int64_t tm = ceil_div(a.M, T::BM), tn = ceil_div(a.N, T::BN);
@@ -292,15 +413,40 @@ hipError_t launch_reg(const GemmArgs &a) {
     return hipGetLastError();
 }
 
+template <int KS>
+hipError_t launch_reg_ks(const GemmArgs &a) {
+    using T = RegSmall;
+    const int64_t tm = ceil_div(a.M, T::BM), tn = ceil_div(a.N, T::BN);
+    const int vec_a = vec4_ok(a.A, a.lda), vec_b = vec4_ok(a.B, a.ldb), vec_c = vec4_ok(a.C, a.ldc);
+    hipLaunchKernelGGL((gemm_regblock_f32_ks<T, KS>), dim3(static_cast<uint32_t>(tm * tn)),
+                       dim3(T::THREADS * KS), 0, a.stream, a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb,
+                       a.C, a.ldc, tm, tn, vec_a, vec_b, vec_c);
+    return hipGetLastError();
+}
+
 }  // namespace
 
-LaunchPlan plan_regblock(int64_t M, int64_t N, int64_t /*K*/) {
+LaunchPlan plan_regblock(int64_t M, int64_t N, int64_t K) {
+    static const char *const ks_names[] = {nullptr, nullptr, "gemm_regblock_f32_ks<64x64, 4x4, K in 2>",
+                                           "gemm_regblock_f32_ks<64x64, 4x4, K in 3>",
+                                           "gemm_regblock_f32_ks<64x64, 4x4, K in 4>"};
+    if (const int ks = split_k_groups(M, N, K)) {
+        LaunchPlan p = plan_reg<RegSmall>(M, N, ks_names[ks]);
+        p.block = RegSmall::THREADS * ks;
+        p.lds_bytes = ks * p.lds_bytes;
+        return p;
+    }
     return small_tiles(M, N) ? plan_reg<RegSmall>(M, N, "gemm_regblock_f32<64x64, 4x4>")
                              : plan_reg<RegLarge>(M, N, "gemm_regblock_f32<128x128, 8x8>");
 }
 
 hipError_t launch_regblock(const GemmArgs &a) {
-    return small_tiles(a.M, a.N) ? launch_reg<RegSmall>(a) : launch_reg<RegLarge>(a);
+    switch (split_k_groups(a.M, a.N, a.K)) {
+        case 4: return launch_reg_ks<4>(a);
+        case 3: return launch_reg_ks<3>(a);
+        case 2: return launch_reg_ks<2>(a);
+        default: return small_tiles(a.M, a.N) ? launch_reg<RegSmall>(a) : launch_reg<RegLarge>(a);
+    }
 }
 
 }  // namespace tra
