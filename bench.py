@@ -238,16 +238,44 @@ def cpu_model():
     return None
 
 
-def cpu_single_thread(w):
-    """One run of the CPU oracle on one thread: the other end of the oracle's
-    scaling, beside the all-core cpu_baseline."""
+# The oracle timed beside each configuration: (workload, timed runs after one
+# warm-up run (0: a single run), also on one thread).  The small shapes take
+# 1 warm-up and 3 timed runs on all cores and on one thread; the large ones
+# one run on all cores (4096^3 is 6.9e10 binary64 multiply-adds: about 20 s
+# on 16 cores).
+ORACLE_CONFIGS = (("int256", 3, True), ("uniform1024", 3, True), ("normal4096", 0, False),
+                  ("ragged", 0, False), ("tall", 0, False))
+
+
+def oracle_configs():
+    """The CPU oracle on every configured shape, beside the GPU numbers: a
+    wall clock around each call, as page "[AutoMine++] #2 matmul trial and
+    error" times its CPU loop (section "Intuitive implementation (by CPU)")."""
     import oracle
-    A, B = w.make()
-    t0 = time.perf_counter()
-    oracle.gemm(A, B, nthreads=1)
-    t = time.perf_counter() - t0
-    return {"threads": 1, "seconds": round(t, 3), "gflops": round(w.flops / t / 1e9, 3),
-            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
+    from tiling_roofline_analysis_amd import inputs
+    every = oracle.default_threads()
+    out = {"host_cpus": os.cpu_count(), "cpu_model": cpu_model(), "threads_all_cores": every,
+           "configs": {}}
+    for name, runs, one_thread in ORACLE_CONFIGS:
+        w = inputs.WORKLOADS[name]
+        A, B = w.make()
+        entry = {"workload": f"{w.M}x{w.N}x{w.K}, {w.what}"}
+        for threads in (every, 1) if one_thread else (every,):
+            if runs:
+                oracle.gemm(A, B, nthreads=threads)   # warm-up, untimed
+            times = []
+            for _ in range(max(1, runs)):
+                t0 = time.perf_counter()
+                oracle.gemm(A, B, nthreads=threads)
+                times.append(time.perf_counter() - t0)
+            t = statistics.median(times)
+            entry[f"threads_{threads}"] = {
+                "runs_s": [round(x, 4) for x in times], "median_s": round(t, 4),
+                "gflops": round(w.flops / t / 1e9, 3)}
+            log(f"[oracle] {name} on {threads} thread(s): {entry[f'threads_{threads}']}")
+        out["configs"][name] = entry
+        del A, B
+    return out
 
 
 def cpu_baseline(w, seconds=10.0):
@@ -292,6 +320,8 @@ def main():
                     help="skip timing the ragged, tall-skinny and per-GPU-slab shapes")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip host-inclusive timing and the torch / numpy comparisons")
+    ap.add_argument("--no-oracle-configs", action="store_true",
+                    help="skip timing the CPU oracle on every configured shape")
     ap.add_argument("--plot", metavar="SVG", help="write the roofline chart of the ladder here")
     ap.add_argument("--plot-table", metavar="MD", help="write the chart's points as a table here")
     args = ap.parse_args()
@@ -380,7 +410,8 @@ def main():
                 "ms_per_step": round(m["avg_ms"], 5), "min_ms": round(m["min_ms"], 5),
                 "frac_of_fp32_peak": round(rep["tflops"] / rl.PEAK_FP32_MFMA_TFLOPS, 4),
                 "frac_of_hbm_floor": round(rep["frac_of_hbm_floor"], 4),
-                "kernel": tra.tra_gemm_describe(tra.AUTO, ws.M, ws.N, ws.K)}
+                "kernel": tra.tra_gemm_describe(tra.AUTO, ws.M, ws.N, ws.K),
+                "traffic": stored_traffic(name)}
     gpu_wall = time.perf_counter() - t_wall
     roofs = None
     if not args.no_roofs:
@@ -463,8 +494,8 @@ def main():
         log("[cpu_baseline] timing the oracle ...")
         line["cpu_baseline"] = cpu_baseline(inputs.WORKLOADS[PRIMARY])
         log(f"[cpu_baseline] {line['cpu_baseline']['value'] * 1e3:.3f} GFLOP/s")
-        line["detail"]["cpu_oracle_1thread"] = cpu_single_thread(inputs.WORKLOADS[PRIMARY])
-        log(f"[cpu_baseline] one thread: {line['detail']['cpu_oracle_1thread']}")
+    if not args.no_oracle_configs:
+        line["detail"]["cpu_oracle"] = oracle_configs()
     print(json.dumps(line), flush=True)
 
 

@@ -128,3 +128,44 @@ def test_counters_summary_ratios(tmp_path):
         assert cells[8] == "0.100"
         assert cells[10] == "1.000"
         assert cells[12] == "0.500"
+
+
+def test_traffic_summary_adds_the_kernels_of_one_call(tmp_path):
+    # a split call launches two kernels (parts and fixup), each dispatched
+    # once per call; torch's own kernels are left out, and the copy scales
+    copy = "__amd_rocclr_copyBuffer"
+    parts = "void tra::(anonymous namespace)::gemm_mfma_f32_parts<tra::Tile<64> >(long)"
+    fixup = "void tra::(anonymous namespace)::gemm_mfma_f32_fixup<tra::Tile<64> >(long)"
+    fetch, write = tmp_path / "f.db", tmp_path / "w.db"
+    _counters_db(fetch, [(copy, 1 << 20, "FETCH_SIZE", profiling.COPY_BYTES / 2048.0, 0.0)]
+                 + [(parts, 1000, "FETCH_SIZE", 300.0, 0.0)] * 12
+                 + [(fixup, 64, "FETCH_SIZE", 20.0, 0.0)] * 12
+                 + [("void at::native::fill_kernel(long)", 64, "FETCH_SIZE", 1e6, 0.0)])
+    _counters_db(write, [(copy, 1 << 20, "WRITE_SIZE", profiling.COPY_BYTES / 1024.0, 0.0)]
+                 + [(parts, 1000, "WRITE_SIZE", 50.0, 0.0)] * 12
+                 + [(fixup, 64, "WRITE_SIZE", 8.0, 0.0)] * 12)
+    text = profiling.traffic_summary(str(fetch), str(write), "ragged", "cmd {counter}", 1000)
+    kv = dict(x.split(" = ") for x in text.splitlines() if " = " in x and not x.startswith("#"))
+    assert kv["calls"] == "12"
+    assert float(kv["hbm_read_bytes_per_launch"]) == pytest.approx(320.0 * 1024 * 2)
+    assert float(kv["hbm_write_bytes_per_launch"]) == pytest.approx(58.0 * 1024)
+    assert float(kv["hbm_bytes_per_launch"]) == pytest.approx(320.0 * 2048 + 58.0 * 1024)
+    assert kv["source_digest"] == profiling.source_digest()
+    assert "cmd FETCH_SIZE" in text and "cmd WRITE_SIZE" in text
+
+
+def test_configs_summary_one_row_per_kernel(tmp_path):
+    db = tmp_path / "c.db"
+    k = "void tra::(anonymous namespace)::gemm_mfma_f32<tra::Tile<64> >(long)"
+    clk = 1000.0
+    v = {"GRBM_GUI_ACTIVE": 8 * clk, "SQ_INSTS_LDS": 400.0, "SQ_LDS_BANK_CONFLICT": 0.0,
+         "SQ_WAIT_INST_LDS": 30.0, "SQ_WAVE_CYCLES": 300.0, "SQ_INSTS_VALU": 5.0,
+         "SQ_INSTS_MFMA": 7.0, "SQ_VALU_MFMA_BUSY_CYCLES": 512.0 * clk}
+    _counters_db(db, [(k, 65536, n, x, 2400.0) for n, x in v.items()]
+                 + [("void at::native::copy(long)", 64, "SQ_INSTS_LDS", 9.0, 1.0)])
+    text = profiling.configs_summary([("tall", str(db))], "the cmd")
+    body = [x for x in text.splitlines() if x.startswith("| tall")]
+    assert len(body) == 1
+    cells = [x.strip() for x in body[0].strip("|").split("|")]
+    assert cells[2:9] == ["65536", "1", "2.4", "0.4", "400", "0.000", "0.100"]
+    assert cells[11] == "0.500"

@@ -12,14 +12,22 @@ This module turns one into the short text summaries kept under profiles/:
   ladder   the same for every rung of the ladder at both configured shapes
            (bench.py run with its ladder), the points of the roofline chart;
   counters SQ instruction, LDS and MFMA counters of every rung from one
-           `--pmc` pass over bench.py's ladder.
+           `--pmc` pass over bench.py's ladder;
+  drive    runs one configured workload through the C ABI (the library's
+           own choice of kernels) a given number of times, after a plain
+           device copy of known size: the program to profile, one workload
+           per process, so that every GEMM kernel in its results belongs to
+           that workload;
+  configs  SQ counters of the kernels of each workload from such runs.
 
 The traffic summary records a digest of the kernel sources; bench.py reports
 the stored traffic only while that digest matches the current sources.
 
     python -m tiling_roofline_analysis_amd.profiling trace DB --cmd "..."
+    python -m tiling_roofline_analysis_amd.profiling drive ragged --reps 20
     python -m tiling_roofline_analysis_amd.profiling traffic FETCH_DB WRITE_DB \\
-        --match "MfmaTile<64, 64" --grid 65536 --workload uniform1024 --cmd "..."
+        --workload ragged --cmd "..."
+    python -m tiling_roofline_analysis_amd.profiling configs --cmd "..." ragged=DB ...
 """
 from __future__ import annotations
 
@@ -144,41 +152,62 @@ def trace_summary(db: str, cmd: str) -> str:
     return "\n".join(out) + "\n"
 
 
-def _counter(db, match, grid):
+def _is_gemm(name: str) -> bool:
+    return "tra::" in name and "gemm_" in name
+
+
+def gemm_kernels(db, counter):
+    """[(kernel name, grid lanes, dispatches, mean value)] of the library's
+    GEMM kernels in a counters database, and the calibration copy's mean
+    reading (the copy of the largest grid)."""
     c = _db(db)
     rows = c.execute(
-        "select kernel_name, grid_size, counter_name, avg(value), count(*) from counters_collection "
-        "group by kernel_name, grid_size, counter_name").fetchall()
-    copy = [r for r in rows if COPY_KERNEL in r[0]]
-    gemm = [r for r in rows if match in r[0] and (grid is None or r[1] == grid)]
-    if not copy or len(gemm) != 1:
-        raise SystemExit(f"{db}: expected one calibration copy and one GEMM kernel "
-                         f"(found {len(copy)} / {len(gemm)})")
-    big = max(copy, key=lambda r: r[1])
-    return gemm[0], big
+        "select kernel_name, grid_size, count(*), avg(value) from counters_collection "
+        "where counter_name = ? group by kernel_name, grid_size", (counter,)).fetchall()
+    copies = [r for r in rows if COPY_KERNEL in r[0]]
+    if not copies:
+        raise SystemExit(f"{db}: no calibration copy ({COPY_KERNEL})")
+    gemm = [r for r in rows if _is_gemm(r[0])]
+    if not gemm:
+        raise SystemExit(f"{db}: no GEMM kernel")
+    return gemm, max(copies, key=lambda r: r[1])[3]
 
 
-def traffic_summary(fetch_db, write_db, match, grid, workload, cmd, algorithmic_bytes):
-    g_f, c_f = _counter(fetch_db, match, grid)
-    g_w, c_w = _counter(write_db, match, grid)
-    fetch_scale = COPY_BYTES / (c_f[3] * 1024.0)
-    write_scale = COPY_BYTES / (c_w[3] * 1024.0)
-    read_b = g_f[3] * 1024.0 * fetch_scale
-    write_b = g_w[3] * 1024.0 * write_scale
+def per_call(kernels):
+    """Counter value per GEMM call: every kernel a call launches is dispatched
+    once per call, so the call count is the largest dispatch count, and each
+    kernel contributes mean x dispatches / calls."""
+    calls = max(n for _, _, n, _ in kernels)
+    return sum(v * n for _, _, n, v in kernels) / calls, calls
+
+
+def traffic_summary(fetch_db, write_db, workload, cmd, algorithmic_bytes):
+    fk, fcopy = gemm_kernels(fetch_db, "FETCH_SIZE")
+    wk, wcopy = gemm_kernels(write_db, "WRITE_SIZE")
+    fetch_scale = COPY_BYTES / (fcopy * 1024.0)
+    write_scale = COPY_BYTES / (wcopy * 1024.0)
+    f_kib, calls = per_call(fk)
+    w_kib, _ = per_call(wk)
+    read_b = f_kib * 1024.0 * fetch_scale
+    write_b = w_kib * 1024.0 * write_scale
     total = read_b + write_b
     lines = [
-        f"# HBM traffic of one GEMM launch from rocprofv3 counters",
+        "# HBM traffic of one GEMM call from rocprofv3 counters",
         f"# FETCH_SIZE pass: {cmd.format(counter='FETCH_SIZE')}",
         f"# WRITE_SIZE pass: {cmd.format(counter='WRITE_SIZE')}",
-        f"# kernel: {g_f[0].replace('(anonymous namespace)::', '').split('(long')[0]}",
-        f"# calibration: plain device copy of {COPY_BYTES} bytes ({c_f[0]}):",
-        f"#   FETCH_SIZE reads {c_f[3]:.1f} KiB -> scale {fetch_scale:.4f};"
-        f" WRITE_SIZE reads {c_w[3]:.1f} KiB -> scale {write_scale:.4f}",
+        f"# calibration: plain device copy of {COPY_BYTES} bytes in the same runs:",
+        f"#   FETCH_SIZE reads {fcopy:.1f} KiB -> scale {fetch_scale:.4f};"
+        f" WRITE_SIZE reads {wcopy:.1f} KiB -> scale {write_scale:.4f}",
+    ]
+    for name, grid, n, v in fk:
+        w = [x for x in wk if x[0] == name and x[1] == grid]
+        lines.append(f"# kernel: {_short(name)} grid_lanes {grid} dispatches {n}: "
+                     f"FETCH_SIZE {v:.1f} KiB, WRITE_SIZE {w[0][3] if w else float('nan'):.1f} KiB")
+    lines += [
         f"workload = {workload}",
-        f"grid_lanes = {g_f[1]}",
-        f"dispatches = {g_f[4]}",
-        f"fetch_size_kib = {g_f[3]:.1f}",
-        f"write_size_kib = {g_w[3]:.1f}",
+        f"calls = {calls}",
+        f"fetch_size_kib = {f_kib:.1f}",
+        f"write_size_kib = {w_kib:.1f}",
         f"fetch_scale = {fetch_scale:.4f}",
         f"write_scale = {write_scale:.4f}",
         f"hbm_read_bytes_per_launch = {read_b:.0f}",
@@ -188,6 +217,79 @@ def traffic_summary(fetch_db, write_db, match, grid, workload, cmd, algorithmic_
         f"traffic_over_algorithmic = {total / algorithmic_bytes:.3f}",
         f"source_digest = {source_digest()}",
     ]
+    return "\n".join(lines) + "\n"
+
+
+def drive(workload: str, reps: int, calibration: bool = True) -> None:
+    """Runs `workload` through gemm_f32 (the library's choice) 2 + reps
+    times on device-resident inputs, after 5 plain device copies of
+    COPY_BYTES bytes (the calibration for FETCH_SIZE and WRITE_SIZE)."""
+    sys.path.insert(0, ROOT)
+    import torch
+    import tiling_roofline_analysis_amd as tra
+    from tiling_roofline_analysis_amd import inputs
+    w = inputs.WORKLOADS[workload]
+    A, B = w.make()
+    dA = torch.from_numpy(A).to("cuda:0")
+    dB = torch.from_numpy(B).to("cuda:0")
+    dC = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda:0")
+    del A, B
+    if calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    h = torch.cuda.current_stream().cuda_stream
+    print(f"[drive] {workload}: {tra.tra_gemm_describe(tra.AUTO, w.M, w.N, w.K)}",
+          file=sys.stderr, flush=True)
+    for _ in range(2 + reps):
+        st = tra.gemm_f32(w.M, w.N, w.K, dA.data_ptr(), w.K, dB.data_ptr(), w.N, dC.data_ptr(),
+                          w.N, h)
+        if st != tra.TRA_OK:
+            raise tra.TraError(st, "gemm_f32")
+    torch.cuda.synchronize()
+    print(f"[drive] {workload}: {2 + reps} calls done", file=sys.stderr, flush=True)
+
+
+def configs_summary(pairs, cmd):
+    """Markdown table of the SQ counters (SQ_COUNTERS) of every GEMM kernel of
+    each workload, from one `--pmc` run of `drive` per workload."""
+    lines = [
+        "# SQ counters per dispatch of each configured workload's kernels (rocprofv3 --pmc)", "",
+        f"Command, once per workload: `{cmd}`", "",
+        "Averages per dispatch. `clk` = GRBM_GUI_ACTIVE / 8 XCDs, the kernel's length in GPU "
+        "clocks. SIMD-clocks = 4 SIMDs x 256 CUs x clk.", "",
+        "| workload | kernel | grid (lanes) | dispatches | duration us | clk/2.4GHz us | "
+        "LDS instr | bank-conflict cycles per LDS instr | LDS wait / wave cycles | VALU instr | "
+        "MFMA instr | MFMA busy / SIMD-clocks |",
+        "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for workload, db in pairs:
+        c = _db(db)
+        rows = c.execute(
+            "select kernel_name, grid_size, counter_name, avg(value), count(*), avg(duration) "
+            "from counters_collection group by kernel_name, grid_size, counter_name").fetchall()
+        kernels = {}
+        for name, grid, cn, v, n, dur in rows:
+            if not _is_gemm(name):
+                continue
+            d = kernels.setdefault((name, grid), {"dispatches": n, "duration_ns": dur})
+            d[cn] = v
+        for (name, grid), d in kernels.items():
+            clk = d.get("GRBM_GUI_ACTIVE", 0.0) / XCDS
+            simd_clk = SIMDS_PER_CU * CUS * clk
+            lds = d.get("SQ_INSTS_LDS", 0.0)
+            conflict = d.get("SQ_LDS_BANK_CONFLICT", 0.0) / lds if lds else 0.0
+            wc = d.get("SQ_WAVE_CYCLES", 0.0)
+            wait = d.get("SQ_WAIT_INST_LDS", 0.0) / wc if wc else 0.0
+            busy = d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / simd_clk if simd_clk else 0.0
+            lines.append(
+                f"| {workload} | `{_short(name)}` | {grid} | {d['dispatches']} | "
+                f"{d['duration_ns'] / 1e3:.1f} | {clk / 2.4e3:.1f} | {lds:.4g} | {conflict:.3f} | "
+                f"{wait:.3f} | {d.get('SQ_INSTS_VALU', 0.0):.4g} | "
+                f"{d.get('SQ_INSTS_MFMA', 0.0):.4g} | {busy:.3f} |")
+    lines += ["", f"sources_digest = {all_sources_digest()}"]
     return "\n".join(lines) + "\n"
 
 
@@ -361,10 +463,15 @@ def main(argv=None):
     f = sub.add_parser("traffic")
     f.add_argument("fetch_db")
     f.add_argument("write_db")
-    f.add_argument("--match", required=True)
-    f.add_argument("--grid", type=int, default=None)
     f.add_argument("--workload", required=True)
     f.add_argument("--cmd", required=True, help="profiling command with {counter}")
+    dr = sub.add_parser("drive")
+    dr.add_argument("workload")
+    dr.add_argument("--reps", type=int, default=20)
+    dr.add_argument("--no-calibration", action="store_true")
+    cf = sub.add_parser("configs")
+    cf.add_argument("--cmd", required=True, help="the profiling command")
+    cf.add_argument("pairs", nargs="+", help="WORKLOAD=DB")
     lad = sub.add_parser("ladder")
     lad.add_argument("fetch_db")
     lad.add_argument("write_db")
@@ -380,12 +487,16 @@ def main(argv=None):
     elif args.what == "ladder":
         sys.path.insert(0, ROOT)
         sys.stdout.write(ladder_summary(args.fetch_db, args.write_db, args.cmd))
+    elif args.what == "drive":
+        drive(args.workload, args.reps, not args.no_calibration)
+    elif args.what == "configs":
+        pairs = [tuple(x.split("=", 1)) for x in args.pairs]
+        sys.stdout.write(configs_summary(pairs, args.cmd))
     else:
         sys.path.insert(0, ROOT)
         from tiling_roofline_analysis_amd import inputs, roofline
         w = inputs.WORKLOADS[args.workload]
-        sys.stdout.write(traffic_summary(args.fetch_db, args.write_db, args.match, args.grid,
-                                         args.workload, args.cmd,
+        sys.stdout.write(traffic_summary(args.fetch_db, args.write_db, args.workload, args.cmd,
                                          roofline.gemm_bytes(w.M, w.N, w.K)))
 
 
