@@ -452,7 +452,7 @@ __host__ __device__ __forceinline__ int64_t part_begin(const PartPlan &p, int j)
 // One pass of the block tile at (c.m0, c.n0) over slices s0 .. s0+n-1
 // (n = 0: a zero tile).  Stores rows [row_lo, rows) and columns
 // [col_lo, cols) of the tile to `out` (its corner, leading dimension ldo).
-template <class T>
+template <class T, bool ALIGNED = false>
 __device__ __forceinline__ void tile_pass(const Ctx<T> &c, int vec_a, int vec_b, float *lds,
                                           int64_t s0, int64_t n, float *out, int64_t ldo,
                                           int row_lo, int64_t rows, int col_lo, int64_t cols) {
@@ -474,7 +474,10 @@ __device__ __forceinline__ void tile_pass(const Ctx<T> &c, int vec_a, int vec_b,
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    if (n > 0) {
+    if (ALIGNED && n > 0) {
+        // the host found every tile inside the matrices with float4 rows
+        k_loop<T, kVec>(c, lds, wm0 + l32, wn0 + l32, kbase, acc, s0, n);
+    } else if (n > 0) {
         const bool inside = (c.m0 + BM <= c.M) && (c.n0 + BN <= c.N);
         // a tile larger than the matrix (M < BM or N < BN) loads whole
         // float4s when its rows are aligned and N is a multiple of 4 (then
@@ -618,8 +621,12 @@ __device__ __forceinline__ void part_fixup(int job, int64_t M, int64_t N, float 
 // The main launch: workgroups [0, sk_tiles * fix_chunks) finish the
 // stream-K tiles (the stream-K launch has completed before this one
 // starts), the rest run one data-parallel tile each.  Without a split
-// (sk_tiles = 0) every workgroup runs one tile.
-template <class T>
+// (sk_tiles = 0) every workgroup runs one tile.  ALIGNED: the host found
+// that every tile lies inside the matrices and loads whole float4s (see
+// aligned_launch), so the kernel holds that load mode's K loop alone --
+// a third of the code, whose first fetch into the instruction cache of
+// every CU is part of each launch's fixed cost (1024^3: 19.59 -> 19.44 us).
+template <class T, bool ALIGNED>
 __global__ __launch_bounds__(T::THREADS)
 void gemm_mfma_f32(int64_t M, int64_t N, int64_t K,
                    const float *__restrict__ A, int64_t lda,
@@ -644,8 +651,8 @@ void gemm_mfma_f32(int64_t M, int64_t N, int64_t K,
     const Ctx<T> c{M, N, K, A, lda, B, ldb, o.m0, o.n0, static_cast<int>(threadIdx.x)};
     const int64_t rows = M - o.m0 < T::BM ? M - o.m0 : T::BM;
     const int64_t cols = N - o.n0 < T::BN ? N - o.n0 : T::BN;
-    tile_pass<T>(c, vec_a, vec_b, lds, 0, p.ipt, C + o.m0 * ldc + o.n0, ldc, o.skip_m, rows,
-                 o.skip_n, cols);
+    tile_pass<T, ALIGNED>(c, vec_a, vec_b, lds, 0, p.ipt, C + o.m0 * ldc + o.n0, ldc, o.skip_m,
+                          rows, o.skip_n, cols);
 }
 
 // The stream-K launch: workgroup w runs slices [sk_begin(w), sk_begin(w+1))
@@ -964,6 +971,15 @@ LaunchPlan plan_for(int64_t M, int64_t N, int64_t K, bool stream_k, const char *
     return p;
 }
 
+// True when every tile of the launch lies inside the matrices (M >= BM and
+// N >= BN, so tile_origin moves the edge tiles inside) and loads float4s:
+// A and B rows 16-byte aligned, and every tile's first column a multiple
+// of 4 (the columns of the moved last tile start at N - BN).
+template <class T>
+bool aligned_launch(const GemmArgs &a, int vec_a, int vec_b) {
+    return vec_a && vec_b && a.M >= T::BM && a.N >= T::BN && (a.N & 3) == 0;
+}
+
 // Launches on the caller's stream: the stream-K runs and then the main
 // launch (which first adds their partial sums), or the parts with the
 // data-parallel tiles and then their fixup, or the main launch alone.
@@ -996,8 +1012,12 @@ hipError_t launch_tile(const GemmArgs &a, bool stream_k, void *ws, size_t ws_byt
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     // fixups of the stream-K tiles, then the data-parallel tiles
-    hipLaunchKernelGGL(gemm_mfma_f32<T>, grid, dim3(T::THREADS), 0, a.stream, a.M, a.N, a.K, a.A,
-                       a.lda, a.B, a.ldb, a.C, a.ldc, p, vec_a, vec_b, vec_c);
+    if (aligned_launch<T>(a, vec_a, vec_b))
+        hipLaunchKernelGGL((gemm_mfma_f32<T, true>), grid, dim3(T::THREADS), 0, a.stream, a.M,
+                           a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, p, vec_a, vec_b, vec_c);
+    else
+        hipLaunchKernelGGL((gemm_mfma_f32<T, false>), grid, dim3(T::THREADS), 0, a.stream, a.M,
+                           a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, p, vec_a, vec_b, vec_c);
     return hipGetLastError();
 }
 
