@@ -247,10 +247,11 @@ ORACLE_CONFIGS = (("int256", 3, True), ("uniform1024", 3, True), ("normal4096", 
                   ("ragged", 0, False), ("tall", 0, False))
 
 
-def oracle_configs():
-    """The CPU oracle on every configured shape, beside the GPU numbers: a
-    wall clock around each call, as page "[AutoMine++] #2 matmul trial and
-    error" times its CPU loop (section "Intuitive implementation (by CPU)")."""
+def cpu_baseline_configs():
+    """Part of the CPU-baseline leg: the CPU oracle on every configured shape,
+    beside the GPU numbers, with a wall clock around each call, as page
+    "[AutoMine++] #2 matmul trial and error" times its CPU loop (section
+    "Intuitive implementation (by CPU)")."""
     import oracle
     from tiling_roofline_analysis_amd import inputs
     every = oracle.default_threads()
@@ -494,8 +495,8 @@ def main():
         log("[cpu_baseline] timing the oracle ...")
         line["cpu_baseline"] = cpu_baseline(inputs.WORKLOADS[PRIMARY])
         log(f"[cpu_baseline] {line['cpu_baseline']['value'] * 1e3:.3f} GFLOP/s")
-    if not args.no_oracle_configs:
-        line["detail"]["cpu_oracle"] = oracle_configs()
+        if not args.no_oracle_configs:
+            line["detail"]["cpu_oracle"] = cpu_baseline_configs()
     print(json.dumps(line), flush=True)
 
 
