@@ -227,6 +227,10 @@ def time_cold(tra, torch, w, dA, dB, dC, launches=20):
             "tflops": round(w.flops / med / 1e9, 3), "launches": len(per)}
 
 
+def shape_label(w):
+    return f"M=N=K={w.M}" if w.M == w.N == w.K else f"M={w.M} N={w.N} K={w.K}"
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as fh:
@@ -247,18 +251,17 @@ ORACLE_CONFIGS = (("int256", 3, True), ("uniform1024", 3, True), ("normal4096", 
                   ("ragged", 0, False), ("tall", 0, False))
 
 
-def cpu_baseline_configs():
+def cpu_baseline_configs(workloads):
     """Part of the CPU-baseline leg: the CPU oracle on every configured shape,
     beside the GPU numbers, with a wall clock around each call, as page
     "[AutoMine++] #2 matmul trial and error" times its CPU loop (section
     "Intuitive implementation (by CPU)")."""
     import oracle
-    from tiling_roofline_analysis_amd import inputs
     every = oracle.default_threads()
     out = {"host_cpus": os.cpu_count(), "cpu_model": cpu_model(), "threads_all_cores": every,
            "configs": {}}
     for name, runs, one_thread in ORACLE_CONFIGS:
-        w = inputs.WORKLOADS[name]
+        w = workloads[name]
         A, B = w.make()
         entry = {"workload": f"{w.M}x{w.N}x{w.K}, {w.what}"}
         for threads in (every, 1) if one_thread else (every,):
@@ -321,6 +324,13 @@ def main():
                     help="skip timing the ragged, tall-skinny and per-GPU-slab shapes")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip host-inclusive timing and the torch / numpy comparisons")
+    ap.add_argument("--config", default=PRIMARY,
+                    help="the headline workload (default %(default)s; the others: "
+                         "int256, const256, int1024, normal4096, ragged, tall, rowslab4096, "
+                         "kslab_tall)")
+    ap.add_argument("--seed", type=int, default=None,
+                    help="seed of the random inputs (A takes SEED, B SEED + 1) in place of "
+                         "each workload's own")
     ap.add_argument("--no-oracle-configs", action="store_true",
                     help="skip timing the CPU oracle on every configured shape")
     ap.add_argument("--plot", metavar="SVG", help="write the roofline chart of the ladder here")
@@ -333,6 +343,8 @@ def main():
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
 
+    import dataclasses
+
     import torch
     import tiling_roofline_analysis_amd as tra
     from tiling_roofline_analysis_amd import inputs
@@ -340,6 +352,15 @@ def main():
     from tiling_roofline_analysis_amd.profiling import (source_digest, stored_ladder_traffic,
                                                         stored_traffic)
 
+    if args.config not in inputs.WORKLOADS:
+        ap.error(f"--config: no workload {args.config!r}")
+    # the workloads, with the random ones reseeded if asked
+    workloads = {name: (dataclasses.replace(w, seed=args.seed, what=f"{w.what.split(' seeds')[0]} "
+                                                                  f"seeds {args.seed}/{args.seed + 1}")
+                        if args.seed is not None and w.seed is not None else w)
+                 for name, w in inputs.WORKLOADS.items()}
+    primary = args.config
+    secondary = None if args.no_secondary or args.config == SECONDARY else SECONDARY
     if not os.path.exists(tra.LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
@@ -348,7 +369,7 @@ def main():
     torch.cuda.set_device(0)
 
     def measure(name, steps, warmup, ladder, cold=False):
-        w = inputs.WORKLOADS[name]
+        w = workloads[name]
         A, B = w.make()
         dA = torch.from_numpy(A).to("cuda:0")
         dB = torch.from_numpy(B).to("cuda:0")
@@ -395,14 +416,14 @@ def main():
         torch.cuda.empty_cache()
 
     t_wall = time.perf_counter()
-    prim = measure(PRIMARY, args.steps, args.warmup, not args.no_ladder, not args.no_cold)
-    sec = None if args.no_secondary else measure(SECONDARY, args.steps, args.warmup,
+    prim = measure(primary, args.steps, args.warmup, not args.no_ladder, not args.no_cold)
+    sec = None if secondary is None else measure(secondary, args.steps, args.warmup,
                                                  not args.no_ladder, not args.no_cold)
     shapes = {}
     if not args.no_shapes:
         # Context beside the headline: the other large shapes and one GPU's
         # share of the two large shapes split over 8 GPUs, each through AUTO.
-        for name in OTHER_SHAPES:
+        for name in (x for x in OTHER_SHAPES if x != primary):
             m = measure(name, args.steps, args.warmup, False)
             ws, rep = m["w"], m["rep"]
             shapes[name] = {
@@ -445,9 +466,9 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"FP32 GEMM M=N=K={w.M} row-major, {w.what}",
+        "config": {"workload": f"FP32 GEMM {shape_label(w)} row-major, {w.what}",
                    "M": w.M, "N": w.N, "K": w.K, "kernel": tra.tra_gemm_describe(tra.AUTO, w.M, w.N, w.K)},
-        "roofline": roofline_obj(prim, PRIMARY),
+        "roofline": roofline_obj(prim, primary),
         "detail": {
             "min_ms": round(prim["min_ms"], 5), "median_ms": round(prim["median_ms"], 5),
             "ai_flop_per_byte": round(prim["rep"]["ai"], 2),
@@ -459,44 +480,44 @@ def main():
         },
     }
     if "cold" in prim:
-        line["detail"]["cold"] = {PRIMARY: prim["cold"]}
+        line["detail"]["cold"] = {primary: prim["cold"]}
         if sec is not None:
-            line["detail"]["cold"][SECONDARY] = sec["cold"]
+            line["detail"]["cold"][secondary] = sec["cold"]
     if prim["ladder"]:
-        line["ladder"] = {PRIMARY: prim["ladder"]}
+        line["ladder"] = {primary: prim["ladder"]}
     if sec is not None:
         ws = sec["w"]
         line["secondary"] = {
-            "workload": f"FP32 GEMM M=N=K={ws.M} row-major, {ws.what}",
+            "workload": f"FP32 GEMM {shape_label(ws)} row-major, {ws.what}",
             "value": round(sec["rep"]["tflops"], 3), "unit": "TFLOP/s",
             "ms_per_step": round(sec["avg_ms"], 5), "min_ms": round(sec["min_ms"], 5),
             "kernel": tra.tra_gemm_describe(tra.AUTO, ws.M, ws.N, ws.K),
-            "roofline": roofline_obj(sec, SECONDARY),
+            "roofline": roofline_obj(sec, secondary),
         }
         if sec["ladder"]:
-            line.setdefault("ladder", {})[SECONDARY] = sec["ladder"]
+            line.setdefault("ladder", {})[secondary] = sec["ladder"]
     if shapes:
         line["shapes"] = shapes
     if not args.no_compare:
         comp = {}
-        for name in (PRIMARY,) + (() if args.no_secondary else (SECONDARY,)):
-            wc = inputs.WORKLOADS[name]
+        for name in (primary,) + (() if secondary is None else (secondary,)):
+            wc = workloads[name]
             comp[name] = {"host_inclusive": host_inclusive(tra, torch, wc),
                           "torch_matmul_fp32": torch_matmul(torch, wc, args.steps)}
             log(f"[{name}] host-inclusive {comp[name]['host_inclusive']}; "
                 f"torch.matmul {comp[name]['torch_matmul_fp32']}")
             torch.cuda.empty_cache()
-        comp[PRIMARY]["numpy_matmul_fp32"] = numpy_matmul(inputs.WORKLOADS[PRIMARY])
-        log(f"[{PRIMARY}] numpy {comp[PRIMARY]['numpy_matmul_fp32']}")
+        comp[primary]["numpy_matmul_fp32"] = numpy_matmul(workloads[primary])
+        log(f"[{primary}] numpy {comp[primary]['numpy_matmul_fp32']}")
         line["detail"]["compare"] = comp
     if args.plot or args.plot_table:
         rl.write_chart(line, stored_ladder_traffic(), args.plot, args.plot_table)
     if not args.no_cpu_baseline:
         log("[cpu_baseline] timing the oracle ...")
-        line["cpu_baseline"] = cpu_baseline(inputs.WORKLOADS[PRIMARY])
+        line["cpu_baseline"] = cpu_baseline(workloads[primary])
         log(f"[cpu_baseline] {line['cpu_baseline']['value'] * 1e3:.3f} GFLOP/s")
         if not args.no_oracle_configs:
-            line["detail"]["cpu_oracle"] = cpu_baseline_configs()
+            line["detail"]["cpu_oracle"] = cpu_baseline_configs(workloads)
     print(json.dumps(line), flush=True)
 
 

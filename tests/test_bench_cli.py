@@ -19,3 +19,11 @@ def test_more_than_one_gpu_exits_with_a_message(argv, world):
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
     assert r.stdout == ""   # no JSON line
+
+
+def test_unknown_config_is_refused_before_the_gpu():
+    r = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--config", "no_such_shape"],
+                       cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "no workload 'no_such_shape'" in r.stderr
+    assert r.stdout == ""
