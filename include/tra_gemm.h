@@ -195,8 +195,10 @@ TRA_API tra_status gemm_f32_variant_ws(int variant,
  * there: calls that may overlap in time on one device (on different
  * streams, or from threads without ordering) race and must be ordered by
  * the caller, e.g. issued on one stream.  Nothing in the array needs to
- * start at zero.  Otherwise the same arguments, results and status codes
- * as gemm_f32_variant.
+ * start at zero.  The first call on each device looks up the array's
+ * device address (hipGetSymbolAddress); a caller that captures graphs
+ * makes one call on each device before capturing.  Otherwise the same
+ * arguments, results and status codes as gemm_f32_variant.
  */
 #define TRA_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
 

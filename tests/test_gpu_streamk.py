@@ -275,9 +275,10 @@ def test_per_thread_default_stream_keeps_one_workspace_per_thread():
 
 def test_graph_capture_takes_the_caller_workspace():
     # while a stream is captured, the library's own scratch is refused (it
-    # would be allocated into the graph); the caller's workspace is
-    # captured, and every replay -- with eager work and synchronisation in
-    # between -- equals the eager result
+    # would be allocated into the graph); the caller's workspace and the
+    # entry point that allocates nothing are captured, and every replay --
+    # with eager work and synchronisation in between -- equals the eager
+    # result
     import torch
     M, N, K = 3000, 2049, 1531
     A, B = dev(inputs.uniform(M, K, 7)), dev(inputs.uniform(K, N, 8))
@@ -285,6 +286,14 @@ def test_graph_capture_takes_the_caller_workspace():
     ws = torch.empty(need // 4, device="cuda:0")
     eager = tra.matmul(A, B, variant=tra.MFMA_STREAMK, workspace=ws).clone()
     C = torch.full((M, N), float("nan"), device="cuda:0")
+    # the entry point that allocates nothing, warmed by one eager call (its
+    # first call on a device looks up the address of its scratch array)
+    C2 = torch.full((M, N), float("nan"), device="cuda:0")
+    h0 = torch.cuda.current_stream().cuda_stream
+    assert tra.gemm_f32_variant_noalloc(tra.MFMA_STREAMK, M, N, K, A.data_ptr(), K, B.data_ptr(),
+                                        N, C2.data_ptr(), N, h0) == tra.TRA_OK
+    torch.cuda.synchronize()
+    assert torch.equal(C2, eager)
     other = torch.empty((M, N), device="cuda:0")
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -295,12 +304,16 @@ def test_graph_capture_takes_the_caller_workspace():
                                        N, C.data_ptr(), N, s.cuda_stream)
         st = tra.gemm_f32_variant_ws(tra.MFMA_STREAMK, M, N, K, A.data_ptr(), K, B.data_ptr(), N,
                                      C.data_ptr(), N, ws.data_ptr(), need, s.cuda_stream)
+        st2 = tra.gemm_f32_variant_noalloc(tra.MFMA_STREAMK, M, N, K, A.data_ptr(), K,
+                                           B.data_ptr(), N, C2.data_ptr(), N, s.cuda_stream)
     assert refused == tra.TRA_ERR_UNSUPPORTED
-    assert st == tra.TRA_OK
+    assert st == tra.TRA_OK and st2 == tra.TRA_OK
     for r in range(3):
         C.fill_(float("nan"))
+        C2.fill_(float("nan"))
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(C, eager), r
+        assert torch.equal(C2, eager), r
         tra.matmul(A, B, other)   # eager work between replays (library workspace)
         torch.cuda.synchronize()
