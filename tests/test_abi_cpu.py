@@ -61,17 +61,31 @@ def test_status_and_variant_names():
 
 
 def test_describe_plans():
+    # the 8-wave tiles: register-staged slices in two LDS buffers
     d = tra.tra_gemm_describe(tra.MFMA, 4096, 4096, 4096)
     assert "gemm_mfma_f32" in d and "tile=256x128x16" in d and "grid=512" in d
-    assert "block=512" in d
-    d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 1024)
-    assert "tile=64x64x16" in d and "4 sets" not in d and "grid=256" in d and "block=256" in d
+    assert "block=512" in d and "4 sets" in d and "lds_bytes=57856" in d
     d = tra.tra_gemm_describe(tra.MFMA, 2048, 2048, 2048)
     assert "tile=128x128x16" in d and "8 waves" in d and "grid=256" in d and "block=512" in d
+    # the 64 x 64 tiles with K a multiple of 16 and aligned rows: direct
+    # loads into 4 (6 for the deep tile) LDS stages of 8448 bytes
+    d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 1024)
+    assert "tile=64x64x16" in d and "4 LDS stages" in d and "grid=256" in d and "block=256" in d
+    assert "lds_bytes=33792" in d
     d = tra.tra_gemm_describe(tra.MFMA, 16384, 64, 16384)
-    assert "tile=64x64x16" in d and "4 sets" in d and "grid=256" in d
+    assert "tile=64x64x16" in d and "6 LDS stages" in d and "grid=256" in d
+    assert "lds_bytes=50688" in d
+    # K not a multiple of 16: register-staged slices, two LDS buffers
     d = tra.tra_gemm_describe(tra.MFMA, 3000, 2049, 1531)
     assert "tile=64x64x16" in d and "4 sets" in d and "grid=1551" in d and "block=256" in d
+    assert "lds_bytes=18944" in d
+    d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 1000)
+    assert "<64x64x16, 4 waves>" in d and "lds_bytes=18944" in d
+    # fewer than 8 slices (2 S): register-staged
+    d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 112)
+    assert "<64x64x16, 4 waves>" in d
+    d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 128)
+    assert "4 LDS stages" in d
     d = tra.tra_gemm_describe(tra.NAIVE, 1024, 1024, 1024)
     assert "gemm_naive_f32" in d and "grid=4096" in d and "block=256" in d
     d = tra.tra_gemm_describe(tra.LDS_TILED, 1024, 1024, 1024)
@@ -319,16 +333,16 @@ def test_auto_choice(shape, rung):
 
 
 @pytest.mark.parametrize("shape,tile", [
-    ((1024, 1024, 1024), "<64x64x16, 4 waves>"),            # K <= 1024
+    ((1024, 1024, 1024), "<64x64x16, 4 waves, 4 LDS stages>"),     # K <= 1024
     ((3000, 2049, 1531), "<64x64x16, 4 waves, 4 sets>"),    # 128x128 would waste the edge
     ((4096, 4096, 4096), "<256x128x16, 8 waves, 4 sets>"),  # 4 tiles of 128x128 a CU
     ((4096, 2048, 1024), "<256x128x16, 8 waves, 4 sets>"),  # exactly 256 tiles of 256x128
     ((2048, 4096, 2048), "<256x128x16, 8 waves, 4 sets>"),
     ((2048, 2048, 2048), "<128x128x16, 8 waves>"),          # one 128x128 tile a CU
-    ((2304, 2304, 2304), "<128x128x16, 8 waves>"),          # 324 tiles, long K
+    ((2304, 2304, 2304), "<128x128x16, 8 waves>"),          # 324 tiles, long K: parts
     ((2000, 2600, 3000), "<128x128x16, 8 waves>"),          # 336 tiles, edges wasted no worse
     ((3000, 3000, 1000), "<64x64x16, 4 waves>"),            # short K stays on 64x64
-    ((3072, 3072, 3072), "<64x64x16, 4 waves, 4 sets>"),    # 576 tiles: 2.25 a CU
+    ((3072, 3072, 3072), "<64x64x16, 4 waves, 6 LDS stages>"),     # 576 tiles: 2.25 a CU
 ])
 def test_auto_tile_class(shape, tile):
     d = tra.tra_gemm_describe(tra.AUTO, *shape)

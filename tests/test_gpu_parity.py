@@ -285,6 +285,54 @@ def test_tile_shapes_with_tails(variant, shape):
     assert_tol(C, ref.c64, ref.s64, f"{M}x{N}x{K}")
 
 
+# Shapes whose main launch stages its slices with direct loads into LDS
+# (64 x 64 tiles, K a multiple of 16, 16-byte-aligned rows, every tile
+# inside the matrices, at least twice as many slices as stages, no split),
+# in both 64 x 64 tile classes, with M and N not multiples of the tile
+# (edge tiles moved inside), at the fewest slices the pipeline takes and one
+# more, and one tile alone: (M, N, K, kernel the MFMA rung plans).  The
+# stream-K form of the same shapes runs register-staged.
+DMA_SHAPES = [
+    (1000, 1000, 1024, "<64x64x16, 4 waves, 4 LDS stages>"),
+    (1000, 1000, 128, "<64x64x16, 4 waves, 4 LDS stages>"),    # 8 slices: the fewest
+    (1000, 1000, 144, "<64x64x16, 4 waves, 4 LDS stages>"),    # 9: one round and a tail
+    (64, 64, 128, "<64x64x16, 4 waves, 4 LDS stages>"),        # one tile
+    (700, 900, 1536, "<64x64x16, 4 waves, 6 LDS stages>"),
+    (64, 64, 1040, "<64x64x16, 4 waves, 6 LDS stages>"),       # 65 slices, one tile
+    (3000, 2052, 1536, "<64x64x16, 4 waves, 6 LDS stages>"),   # 1551 tiles
+    (200, 300, 4112, "<64x64x16, 4 waves, 6 LDS stages>"),     # 20 tiles, long K
+]
+
+
+@pytest.mark.parametrize("shape", DMA_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}x{s[2]}")
+@pytest.mark.parametrize("variant", [tra.MFMA, tra.MFMA_STREAMK, tra.AUTO],
+                         ids=["mfma", "mfma_streamk", "auto"])
+def test_direct_load_staging(variant, shape):
+    M, N, K, kernel = shape
+    assert f"kernel=gemm_mfma_f32{kernel} " in tra.tra_gemm_describe(tra.MFMA, M, N, K)
+    log(f"[case] direct loads {tra.tra_gemm_variant_name(variant)} {M}x{N}x{K}")
+    A, B, ref = tile_shape_case(M, N, K)
+    C, *_ = run_gpu(variant, A, B)
+    assert_tol(C, ref.c64, ref.s64, f"{M}x{N}x{K}")
+    Ai = inputs.small_ints(M, K, 3 * M + K)
+    Bi = inputs.small_ints(K, N, 5 * N + K)
+    Ci, *_ = run_gpu(variant, Ai, Bi)
+    assert_exact(Ci, oracle.gemm(Ai, Bi).c32, f"small ints {M}x{N}x{K}")
+
+
+def test_direct_load_staging_with_padded_rows():
+    # leading dimensions above the row length that keep rows 16-byte
+    # aligned still take the direct loads; C's odd ldc is only stored to
+    M, N, K = 1000, 1000, 1024
+    A, B, ref = tile_shape_case(M, N, K)
+    for variant in (tra.MFMA, tra.AUTO):
+        log(f"[case] direct loads, padded rows, {tra.tra_gemm_variant_name(variant)}")
+        C, buf, ldc, off = run_gpu(variant, A, B, lda=K + 12, ldb=N + 4, ldc=N + 3)
+        assert_tol(C, ref.c64, ref.s64, "padded rows")
+        pad = buf[off:off + M * ldc].reshape(M, ldc)[:, N:]
+        assert (pad == C_SENTINEL).all(), "C written past its rows"
+
+
 # Shapes that send the register-blocked rung to its K split inside the
 # workgroup (4, 3 or 2 lane groups each running an equal share of the K
 # slices), with tails on every axis: (M, N, K, lane groups).

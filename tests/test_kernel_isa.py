@@ -87,3 +87,44 @@ def test_mfma_register_budgets(asm):
                     budget = max(budget, 168)    # planned at three a CU
                 assert vgprs <= budget, f"{name}: {vgprs} VGPRs, plan assumes <= {budget}"
     assert seen == set(VGPR_BUDGET)
+
+
+def _functions(text: str):
+    """name -> assembly body of every kernel function."""
+    out = {}
+    for m in re.finditer(r"^(_Z\S+):\s*;\s*@\1\n(.*?)^\s+s_endpgm", text, re.M | re.S):
+        out.setdefault(m.group(1), m.group(2))
+    return out
+
+
+def _loops(body: str):
+    """The instruction text of each loop: from a loop header label to the
+    branch back to it."""
+    loops = []
+    for m in re.finditer(r"^(\.LBB\w+):[^\n]*Loop Header", body, re.M):
+        label = m.group(1)
+        end = re.search(rf"^\s+s_cbranch\w*\s+{re.escape(label)}\s*$", body[m.end():], re.M)
+        if end:
+            loops.append(body[m.end():m.end() + end.end()])
+    return loops
+
+
+def test_direct_load_loops_keep_loads_in_flight(asm):
+    # The direct-load kernels (gemm_mfma_f32<T, true, true>) stage slices
+    # with global_load_lds_dwordx4 and wait for them with explicit counts.
+    # Their main loop must not wait for every load in flight (vmcnt(0)):
+    # that is what the compiler inserts before an LDS read that may alias
+    # an earlier direct load, and it would serialise the pipeline.
+    funcs = {n: b for n, b in _functions(asm["gemm_mfma.hip"]).items()
+             if n.startswith("_ZN3tra12_GLOBAL__N_113gemm_mfma_f32INS0_8MfmaTile")
+             and n.endswith("Lb1ELb1EEEvlllPKflS5_lPflNS0_6SkPlanEiii")}
+    assert len(funcs) == 2, sorted(funcs)   # the two 64 x 64 tiles
+    for name, body in funcs.items():
+        code = "\n".join(line.split(";")[0] for line in body.splitlines())
+        assert "global_load_lds_dwordx4" in code, name
+        main = [lp for lp in _loops(body) if "global_load_lds_dwordx4" in lp
+                and "v_mfma_f32_32x32x2_f32" in lp]
+        assert main, f"{name}: no loop with direct loads and MFMAs"
+        lp = "\n".join(line.split(";")[0] for line in main[0].splitlines())
+        assert "vmcnt(0)" not in lp, f"{name}: main loop waits for every load in flight"
+        assert re.search(r"s_waitcnt vmcnt\([1-9]\d*\) lgkmcnt\(0\)", lp), name

@@ -42,6 +42,13 @@
 // iteration overlaps that iteration's MFMAs; the memory instructions are
 // issued between the MFMAs (il_order) rather than in bursts.
 //
+// Direct staging (k_loop_dma): where every slice is full and every load an
+// aligned float4 inside the matrices -- the common case of contiguous
+// operands with K a multiple of 16 -- the slices go from global memory
+// straight into a ring of S LDS stages (global_load_lds_dwordx4), with no
+// register sets and no LDS stores; the layout and the waits are described
+// at Dma below.
+//
 // Global loads: a tile that would cross row M or column N is moved back
 // inside the matrices (its rows and columns shared with the neighbouring
 // tile are not stored), so full slices load without checks: float4 loads
@@ -389,6 +396,236 @@ __device__ __forceinline__ void k_loop(const Ctx<T> &c, float *lds, int arow, in
     tail(0);
 }
 
+// ---- direct staging: global memory to LDS without registers ----
+//
+// gfx950's global_load_lds_dwordx4 writes 16 bytes per lane straight into
+// LDS, lane i of a wave at byte 16 i past a wave-uniform base (M0): the
+// data lands in no register, needs no ds_write and no wait before one.
+// Each instruction moves 1 KB per wave, so a slice is laid out in 1 KB
+// blocks:
+//   A block: 16 rows of the slice, 4 quads a row (rows 16 words apart);
+//            quad q of row m is stored at position q ^ ((m >> 2) & 3), so
+//            the 16 rows that 16 consecutive lanes read at one quad
+//            (ds_read_b128) start in 16 distinct 4-bank groups;
+//   B block: 256 / BN rows of BN words; blocks are 256 + PADB words apart,
+//            so the two lane halves, which read rows k and k + BK/2 of the
+//            slice, fall in opposite halves of the 64 banks.
+// Which global quad a lane loads is chosen to fit that layout: four
+// consecutive lanes still read one row's 64 contiguous bytes of A, sixteen
+// (BN = 64) or thirty-two (BN = 128) one row's bytes of B.
+//
+// S stages, each a __shared__ array of its own (so the compiler can tell
+// them apart and does not make a fragment read wait for the loads still in
+// flight into other stages); slice s lives in stage s % S.  Iteration s
+// reads the fragments of slice s+1, runs the MFMAs of slice s and issues
+// the loads of slice s+S into the stage of slice s (free: its fragments
+// were read in iteration s-1, before the barrier that ended it).  It ends
+// by waiting for this wave's loads of slice s+2 and a workgroup barrier,
+// after which every wave's share of slice s+2 is in LDS and every wave has
+// read the fragments of slice s+1.  S-2 slices stay in flight across a
+// barrier: 2 for the Many tile, 4 for the Deep tile, whose shapes stream A
+// from HBM (16384 x 64 x 16384 lost 23% against the register path with 4
+// stages; 6 stages also keep three workgroups a CU, as the register-staged
+// Deep kernel has, where 8 would allow two).  The Many tile lost 2% with 6.
+// Timed against the register path (medians of interleaved rounds, two
+// boxes): 1024^3 +1.2 to +2.3%, 1024^2 x 512 +1.6%, 3072^2 x 2048 +2.7%,
+// 1536 x 2048 x 2048 +1.8%, 16384 x 64 x 16384 +0.3%.  The 8-wave tiles
+// keep the register path: their loop already runs at 98% of the MFMA rate
+// at 4096^3 (direct loads: within 0.2%), and the 128 x 128 tile's ring
+// would let two workgroups share a CU where its registers allow one
+// (2048^3 and 2560^3 1% slower).
+template <class T>
+struct Dma {
+    static constexpr bool USED = T::BM == 64;               // the 64 x 64 tiles only
+    static constexpr int S = T::NR == 4 ? 6 : 4;            // stages
+    static constexpr int RPB = 256 / T::BN;                 // B rows per block
+    static constexpr int PADB = 32 * RPB / T::HALF;         // words between B blocks
+    static constexpr int A_WORDS = T::BM * T::BK;
+    static constexpr int B_BLOCK = 256 + PADB;
+    static constexpr int B_WORDS = T::BK / RPB * B_BLOCK;
+    static constexpr int STAGE = A_WORDS + B_WORDS;         // words per stage
+    static constexpr int A_INS = T::BM * T::BK / 4 / T::THREADS;   // per wave and slice
+    static constexpr int B_INS = T::BK * T::BN / 4 / T::THREADS;
+    static constexpr int NV = A_INS + B_INS;
+    static_assert(!USED || (T::BK == 16 && 256 % T::BN == 0 && T::HALF % RPB == 0),
+                  "block layout");
+    static_assert(!USED || (A_INS >= 1 && B_INS >= 1 && A_INS * T::THREADS * 4 == T::BM * T::BK &&
+                            B_INS * T::THREADS * 4 == T::BK * T::BN),
+                  "every wave moves whole blocks");
+    static_assert(T::WM % 16 == 0, "a lane's rows share (row >> 2) & 3");
+    static_assert((S - 2) * NV < 64 && S >= 4 && S <= 8 && S % 2 == 0,
+                  "vmcnt range, stage arrays, fragment buffers alternate");
+};
+
+// s_waitcnt vmcnt(VM) lgkmcnt(0), expcnt not waited for (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
+}
+
+// The end of a direct-load iteration: this wave's loads older than the
+// last VM are in LDS and its LDS reads are done; then the workgroup
+// barrier.  (__syncthreads would wait for every direct load in flight.)
+// The empty asm keeps the compiler from moving memory accesses across it.
+template <int VM>
+__device__ __forceinline__ void dma_sync() {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm_lgkm0<VM>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <class T>
+struct DmaLane {
+    const float *pa[Dma<T>::A_INS];   // this lane's A quad of slice 0, per instruction
+    const float *pb[Dma<T>::B_INS];   // this lane's B quad of slice 0
+    int wa, wb;                       // the wave's first A and B block in a stage (words)
+    int ra, rb;                       // this lane's fragment offsets in a stage (words)
+};
+
+template <class T>
+__device__ __forceinline__ DmaLane<T> dma_lane(const Ctx<T> &c, int arow, int bcol, int kbase) {
+    using D = Dma<T>;
+    DmaLane<T> d;
+    const int lane = c.t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(c.t >> 6);
+#pragma unroll
+    for (int i = 0; i < D::A_INS; ++i) {
+        const int g = (i * T::WAVES + wave) * 64 + lane;   // float4 of the slice's A
+        const int m = g >> 2, q = (g & 3) ^ ((m >> 2) & 3);
+        d.pa[i] = c.A + (c.m0 + m) * c.lda + 4 * q;
+    }
+#pragma unroll
+    for (int i = 0; i < D::B_INS; ++i) {
+        const int g = (i * T::WAVES + wave) * 64 + lane;   // float4 of the slice's B
+        const int k = g / (T::BN / 4), nq = g % (T::BN / 4);
+        d.pb[i] = c.B + k * c.ldb + c.n0 + 4 * nq;
+    }
+    d.wa = wave * 256;
+    d.wb = D::A_WORDS + wave * D::B_BLOCK;
+    d.ra = arow * 16;
+    d.rb = D::A_WORDS + (kbase / D::RPB) * D::B_BLOCK + (kbase % D::RPB) * T::BN + bcol;
+    return d;
+}
+
+// Issues the direct loads of the slice starting at k0 into a stage.
+template <class T>
+__device__ __forceinline__ void dma_issue(const DmaLane<T> &d, float *stage, int64_t k0,
+                                          int64_t ldb) {
+    using D = Dma<T>;
+#pragma unroll
+    for (int i = 0; i < D::A_INS; ++i)
+        __builtin_amdgcn_global_load_lds(d.pa[i] + k0, stage + d.wa + i * T::WAVES * 256, 16, 0,
+                                         0);
+#pragma unroll
+    for (int i = 0; i < D::B_INS; ++i)
+        __builtin_amdgcn_global_load_lds(d.pb[i] + k0 * ldb,
+                                         stage + d.wb + i * T::WAVES * D::B_BLOCK, 16, 0, 0);
+}
+
+// A lane's fragments of the slice in a stage: A rows arow + 32 i, k quads
+// kbase / 4 + qq (stored at quad position ^ ((row >> 2) & 3), which is the
+// same for all of the lane's rows); B rows kbase + q, columns bcol + 32 j.
+template <class T>
+__device__ __forceinline__ void dma_frags(const DmaLane<T> &d, const float *stage, int kbase,
+                                          Frag<T> &fr) {
+    using D = Dma<T>;
+    const int x = (static_cast<int>(threadIdx.x) >> 2) & 3;
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+#pragma unroll
+        for (int qq = 0; qq < T::HALF / 4; ++qq) {
+            const int pos = ((kbase >> 2) + qq) ^ x;
+            const float4 v =
+                *reinterpret_cast<const float4 *>(stage + d.ra + 32 * 16 * i + 4 * pos);
+            fr.a[i][4 * qq + 0] = v.x;
+            fr.a[i][4 * qq + 1] = v.y;
+            fr.a[i][4 * qq + 2] = v.z;
+            fr.a[i][4 * qq + 3] = v.w;
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < T::HALF; ++q)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j)
+            fr.b[q][j] = stage[d.rb + (q / D::RPB) * D::B_BLOCK + (q % D::RPB) * T::BN + 32 * j];
+}
+
+// Issue order of a direct-load iteration: each MFMA followed by a share of
+// the fragment reads (first half of the MFMAs) or of the direct loads
+// (second half), as il_order does for the register path.
+template <int I, int NM, int RPM, int VPM>
+__device__ __forceinline__ void dma_schedule() {
+    if constexpr (I < NM) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+        if constexpr (I < NM / 2)
+            __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);    // LDS reads
+        else
+            __builtin_amdgcn_sched_group_barrier(0x010, VPM, 0);    // direct loads
+        dma_schedule<I + 1, NM, RPM, VPM>();
+    }
+}
+
+template <class T>
+__device__ __forceinline__ void dma_order() {
+    constexpr int NM = T::HALF * T::FM * T::FN;
+    constexpr int FIRST = NM / 2, SECOND = NM - NM / 2;
+    constexpr int NDR = T::FM * (T::HALF / 4) + (T::HALF * T::FN + 1) / 2;
+    dma_schedule<0, NM, (NDR + FIRST - 1) / FIRST, (Dma<T>::NV + SECOND - 1) / SECOND>();
+}
+
+// The K loop over the n slices of a tile when every slice is full and
+// every load is an aligned float4 inside the matrices (K a multiple of BK,
+// A and B rows 16-byte aligned, the tile inside), n >= 2 S.  stg: the S
+// stage arrays.
+template <class T>
+__device__ __forceinline__ void k_loop_dma(const Ctx<T> &c, float *const *stg, int arow,
+                                           int bcol, int kbase, f32x16 (&acc)[T::FM][T::FN],
+                                           int64_t n) {
+    using D = Dma<T>;
+    constexpr int S = D::S, BK = T::BK;
+    const DmaLane<T> d = dma_lane<T>(c, arow, bcol, kbase);
+    Frag<T> fr[2];
+    // prologue: slices 0 .. S-1 in flight; wait for 0 and 1, read the
+    // fragments of 0, and let every wave finish that read before
+    // iteration 0 reloads stage 0
+#pragma unroll
+    for (int j = 0; j < S; ++j) dma_issue<T>(d, stg[j], j * BK, c.ldb);
+    dma_sync<(S - 2) * D::NV>();
+    dma_frags<T>(d, stg[0], kbase, fr[0]);
+    dma_sync<(S - 2) * D::NV>();
+    int64_t s = 0;
+    for (; s + S - 1 + S < n; s += S) {
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            __builtin_amdgcn_sched_barrier(0);
+            dma_frags<T>(d, stg[(u + 1) % S], kbase, fr[(u + 1) & 1]);
+            mfmas<T, 0, T::HALF>(fr[u & 1], acc);
+            dma_issue<T>(d, stg[u], (s + u + S) * BK, c.ldb);
+            dma_order<T>();
+            dma_sync<(S - 2) * D::NV>();
+        }
+    }
+    // the last iterations: loads only while slices remain, and each waits
+    // for all of this wave's loads
+    for (; s < n; s += S) {
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            if (s + u < n) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (s + u + 1 < n) dma_frags<T>(d, stg[(u + 1) % S], kbase, fr[(u + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                mfmas<T, 0, T::HALF>(fr[u & 1], acc);
+                if (s + u + S < n) dma_issue<T>(d, stg[u], (s + u + S) * BK, c.ldb);
+                dma_sync<0>();
+            }
+        }
+    }
+}
+
 // How the work of one launch is cut up.  Logical tiles [0, sk_tiles) --
 // the last partial wave of tiles -- are shared out by K slice
 // ("stream-K"): their tiles x ipt slices are split into sk_wgs contiguous
@@ -452,10 +689,13 @@ __host__ __device__ __forceinline__ int64_t part_begin(const PartPlan &p, int j)
 // One pass of the block tile at (c.m0, c.n0) over slices s0 .. s0+n-1
 // (n = 0: a zero tile).  Stores rows [row_lo, rows) and columns
 // [col_lo, cols) of the tile to `out` (its corner, leading dimension ldo).
-template <class T, bool ALIGNED = false>
+// DMA: the host found every slice full with aligned float4 rows inside the
+// matrices (dma_launch); stg then holds the direct-load stages.
+template <class T, bool ALIGNED = false, bool DMA = false>
 __device__ __forceinline__ void tile_pass(const Ctx<T> &c, int vec_a, int vec_b, float *lds,
                                           int64_t s0, int64_t n, float *out, int64_t ldo,
-                                          int row_lo, int64_t rows, int col_lo, int64_t cols) {
+                                          int row_lo, int64_t rows, int col_lo, int64_t cols,
+                                          float *const *stg = nullptr) {
     constexpr int BM = T::BM, BN = T::BN, WM = T::WM, WN = T::WN;
     constexpr int FM = T::FM, FN = T::FN;
 
@@ -474,7 +714,9 @@ __device__ __forceinline__ void tile_pass(const Ctx<T> &c, int vec_a, int vec_b,
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    if (ALIGNED && n > 0) {
+    if (DMA) {
+        k_loop_dma<T>(c, stg, wm0 + l32, wn0 + l32, kbase, acc, n);
+    } else if (ALIGNED && n > 0) {
         // the host found every tile inside the matrices with float4 rows
         k_loop<T, kVec>(c, lds, wm0 + l32, wn0 + l32, kbase, acc, s0, n);
     } else if (n > 0) {
@@ -626,7 +868,10 @@ __device__ __forceinline__ void part_fixup(int job, int64_t M, int64_t N, float 
 // aligned_launch), so the kernel holds that load mode's K loop alone --
 // a third of the code, whose first fetch into the instruction cache of
 // every CU is part of each launch's fixed cost (1024^3: 19.59 -> 19.44 us).
-template <class T, bool ALIGNED>
+// DMA: in addition every slice is full (dma_launch), and the K loop stages
+// the slices with direct loads (k_loop_dma) in S stage arrays instead of
+// the two register-staged buffers.
+template <class T, bool ALIGNED, bool DMA = false>
 __global__ __launch_bounds__(T::THREADS)
 void gemm_mfma_f32(int64_t M, int64_t N, int64_t K,
                    const float *__restrict__ A, int64_t lda,
@@ -634,8 +879,26 @@ void gemm_mfma_f32(int64_t M, int64_t N, int64_t K,
                    float *__restrict__ C, int64_t ldc, SkPlan p, int vec_a, int vec_b,
                    int vec_c)
 {
-    __shared__ __attribute__((aligned(16))) float lds[T::LDS_WORDS];
-    lds_poison(lds, T::LDS_WORDS);
+    static_assert(!DMA || (ALIGNED && Dma<T>::USED), "direct loads: aligned 64 x 64 tiles");
+    constexpr int WORDS = DMA ? 4 : T::LDS_WORDS;
+    constexpr int SN = DMA ? Dma<T>::S : 0;
+    constexpr int STAGE = DMA ? Dma<T>::STAGE : 4;
+    __shared__ __attribute__((aligned(16))) float lds[WORDS];
+    __shared__ __attribute__((aligned(16))) float st0[0 < SN ? STAGE : 4];
+    __shared__ __attribute__((aligned(16))) float st1[1 < SN ? STAGE : 4];
+    __shared__ __attribute__((aligned(16))) float st2[2 < SN ? STAGE : 4];
+    __shared__ __attribute__((aligned(16))) float st3[3 < SN ? STAGE : 4];
+    __shared__ __attribute__((aligned(16))) float st4[4 < SN ? STAGE : 4];
+    __shared__ __attribute__((aligned(16))) float st5[5 < SN ? STAGE : 4];
+    __shared__ __attribute__((aligned(16))) float st6[6 < SN ? STAGE : 4];
+    __shared__ __attribute__((aligned(16))) float st7[7 < SN ? STAGE : 4];
+    float *const stg[8] = {st0, st1, st2, st3, st4, st5, st6, st7};
+    if constexpr (DMA) {
+#pragma unroll
+        for (int j = 0; j < SN; ++j) lds_poison(stg[j], STAGE);
+    } else {
+        lds_poison(lds, WORDS);
+    }
 
     const int bid = static_cast<int>(blockIdx.x);
     const int fix = p.sk_tiles * fix_chunks<T>();
@@ -651,8 +914,8 @@ void gemm_mfma_f32(int64_t M, int64_t N, int64_t K,
     const Ctx<T> c{M, N, K, A, lda, B, ldb, o.m0, o.n0, static_cast<int>(threadIdx.x)};
     const int64_t rows = M - o.m0 < T::BM ? M - o.m0 : T::BM;
     const int64_t cols = N - o.n0 < T::BN ? N - o.n0 : T::BN;
-    tile_pass<T, ALIGNED>(c, vec_a, vec_b, lds, 0, p.ipt, C + o.m0 * ldc + o.n0, ldc, o.skip_m,
-                          rows, o.skip_n, cols);
+    tile_pass<T, ALIGNED, DMA>(c, vec_a, vec_b, lds, 0, p.ipt, C + o.m0 * ldc + o.n0, ldc,
+                               o.skip_m, rows, o.skip_n, cols, stg);
 }
 
 // The stream-K launch: workgroup w runs slices [sk_begin(w), sk_begin(w+1))
@@ -953,17 +1216,31 @@ int64_t main_grid(const Split &r) {
            static_cast<int64_t>(r.sk.sk_tiles) * (extra - 1);
 }
 
+// True when every tile lies inside the matrices with float4 rows
+// (aligned_launch) and every slice is full, with enough slices for the
+// direct-load pipeline: the main launch then stages with direct loads.
+inline bool dma_ok(bool aligned, int64_t K, int64_t bk, int64_t stages) {
+    return aligned && K % bk == 0 && K / bk >= 2 * stages;
+}
+
+// `name`, or `dma_name` when the main launch stages with direct loads
+// (planned for 16-byte-aligned operands with lda = K, ldb = N, and only for
+// launches without a split, see launch_tile).
 template <class T>
-LaunchPlan plan_for(int64_t M, int64_t N, int64_t K, bool stream_k, const char *name) {
+LaunchPlan plan_for(int64_t M, int64_t N, int64_t K, bool stream_k, const char *name,
+                    const char *dma_name) {
     const Split r = plan_split<T>(M, N, K, stream_k);
+    const bool aligned = (K & 3) == 0 && M >= T::BM && N >= T::BN && (N & 3) == 0;
+    const bool dma = Dma<T>::USED && r.sk.sk_tiles == 0 && dma_ok(aligned, K, T::BK, Dma<T>::S);
     LaunchPlan p{};
-    p.kernel = name;
+    p.kernel = dma ? dma_name : name;
     p.bm = T::BM;
     p.bn = T::BN;
     p.bk = T::BK;
     p.grid = main_grid<T>(r);
     p.block = T::THREADS;
-    p.lds_bytes = static_cast<int>(T::LDS_WORDS * sizeof(float));
+    p.lds_bytes = static_cast<int>((dma ? Dma<T>::S * Dma<T>::STAGE : T::LDS_WORDS) *
+                                   sizeof(float));
     p.sk_tiles = r.sk.sk_tiles;
     p.sk_wgs = split_wgs(r);
     p.split = r.pp.parts > 0 ? "parts" : (r.sk.sk_wgs > 0 ? "runs" : "none");
@@ -1011,8 +1288,22 @@ hipError_t launch_tile(const GemmArgs &a, bool stream_k, void *ws, size_t ws_byt
                            a.C, a.ldc, p, vec_a, vec_b);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    // fixups of the stream-K tiles, then the data-parallel tiles
-    if (aligned_launch<T>(a, vec_a, vec_b))
+    // fixups of the stream-K tiles, then the data-parallel tiles.  Direct
+    // loads only without a split: their stage ring changes how many
+    // workgroups a CU holds (two 128 x 128 tiles where the register-staged
+    // kernel's registers allow one, two 64 x 64 deep tiles where they allow
+    // three), and the stream-K plan counts on the register-staged kernel's
+    // (2560^3 with stream-K runs: 256 -> 402 us with direct loads)
+    const bool aligned = aligned_launch<T>(a, vec_a, vec_b);
+    if constexpr (Dma<T>::USED) {
+        if (p.sk_tiles == 0 && dma_ok(aligned, a.K, T::BK, Dma<T>::S)) {
+            hipLaunchKernelGGL((gemm_mfma_f32<T, true, true>), grid, dim3(T::THREADS), 0,
+                               a.stream, a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, p,
+                               vec_a, vec_b, vec_c);
+            return hipGetLastError();
+        }
+    }
+    if (aligned)
         hipLaunchKernelGGL((gemm_mfma_f32<T, true>), grid, dim3(T::THREADS), 0, a.stream, a.M,
                            a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, p, vec_a, vec_b, vec_c);
     else
@@ -1027,14 +1318,17 @@ LaunchPlan plan_mfma(int64_t M, int64_t N, int64_t K, bool stream_k) {
     switch (pick(M, N, K)) {
         case Shape::kLarge:
             return plan_for<TileLarge>(M, N, K, stream_k,
-                                       "gemm_mfma_f32<256x128x16, 8 waves, 4 sets>");
+                                       "gemm_mfma_f32<256x128x16, 8 waves, 4 sets>", nullptr);
         case Shape::kMid:
-            return plan_for<TileMid>(M, N, K, stream_k, "gemm_mfma_f32<128x128x16, 8 waves>");
+            return plan_for<TileMid>(M, N, K, stream_k, "gemm_mfma_f32<128x128x16, 8 waves>",
+                                     nullptr);
         case Shape::kMany:
-            return plan_for<TileMany>(M, N, K, stream_k, "gemm_mfma_f32<64x64x16, 4 waves>");
+            return plan_for<TileMany>(M, N, K, stream_k, "gemm_mfma_f32<64x64x16, 4 waves>",
+                                      "gemm_mfma_f32<64x64x16, 4 waves, 4 LDS stages>");
         default:
             return plan_for<TileDeep>(M, N, K, stream_k,
-                                      "gemm_mfma_f32<64x64x16, 4 waves, 4 sets>");
+                                      "gemm_mfma_f32<64x64x16, 4 waves, 4 sets>",
+                                      "gemm_mfma_f32<64x64x16, 4 waves, 6 LDS stages>");
     }
 }
 
