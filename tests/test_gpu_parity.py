@@ -575,6 +575,40 @@ def test_random_shapes_small_ints_exact(variant):
         assert np.all(full[:, N:] == C_SENTINEL), "wrote past column N"
 
 
+def _random_direct_load_shapes(seed, n):
+    # shapes whose MFMA launch stages with direct loads: M, N >= 64, N a
+    # multiple of 4, K a multiple of 16 with at least 8 slices (4 stages,
+    # K <= 1024) or more than 64 (6 stages); leading dimensions padded by
+    # whole quads, so rows stay 16-byte aligned
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M = int(rng.integers(64, 700))
+        N = 4 * int(rng.integers(16, 175))
+        K = 16 * int(rng.integers(8, 65) if i % 2 == 0 else rng.integers(65, 100))
+        pads = tuple(4 * int(x) for x in rng.integers(0, 3, size=3))
+        out.append((M, N, K, pads))
+    return out
+
+
+@pytest.mark.parametrize("variant", [tra.AUTO, tra.MFMA], ids=["auto", "mfma"])
+def test_random_direct_load_shapes_exact(variant):
+    """Seeded random shapes through the direct-load K loop (both stage
+    counts, edge tiles moved inside, padded rows): exact on small integers,
+    and C untouched past column N."""
+    for M, N, K, (pa, pb, pc) in _random_direct_load_shapes(77, 16):
+        assert "LDS stages" in tra.tra_gemm_describe(tra.MFMA, M, N, K), (M, N, K)
+        log(f"[case] direct loads {tra.tra_gemm_variant_name(variant)} {M}x{N}x{K} "
+            f"pads {pa},{pb},{pc}")
+        A = inputs.small_ints(M, K, M * 31 + K)
+        B = inputs.small_ints(K, N, N * 31 + K + 1)
+        ref = oracle.gemm(A, B)
+        C, buf, ldc, off = run_gpu(variant, A, B, K + pa, N + pb, N + pc)
+        assert_exact(C, ref.c32, f"{M}x{N}x{K}")
+        full = buf[off:off + M * ldc].reshape(M, ldc)
+        assert np.all(full[:, N:] == C_SENTINEL), "wrote past column N"
+
+
 @pytest.mark.parametrize("shape", [(150, 130, 70), (300, 500, 203), (40, 2000, 64)],
                          ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("variant", RUNGS + [tra.AUTO], ids=RUNG_IDS + ["auto"])
