@@ -81,10 +81,10 @@ def test_describe_plans():
     assert "lds_bytes=18944" in d
     d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 1000)
     assert "<64x64x16, 4 waves>" in d and "lds_bytes=18944" in d
-    # fewer than 8 slices (2 S): register-staged
-    d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 112)
+    # fewer than 32 slices: register-staged
+    d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 496)
     assert "<64x64x16, 4 waves>" in d
-    d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 128)
+    d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 512)
     assert "4 LDS stages" in d
     d = tra.tra_gemm_describe(tra.NAIVE, 1024, 1024, 1024)
     assert "gemm_naive_f32" in d and "grid=4096" in d and "block=256" in d

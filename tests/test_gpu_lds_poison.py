@@ -41,7 +41,7 @@ SHAPES = [
     (1000, 1000, 1007),   # register-blocked rung: K split over 3 lane groups, K tail
     (300, 700, 255),      # register-blocked rung: K split over 4 lane groups
     (100, 200, 127),      # register-blocked rung: K split over 2 lane groups
-    (1000, 1000, 144),    # direct loads into LDS, 64 x 64, 4 stages
+    (1000, 1000, 528),    # direct loads into LDS, 64 x 64, 4 stages
     (700, 900, 1536),     # direct loads, 64 x 64, 6 stages
     (64, 64, 1040),       # direct loads, one tile
     (200, 300, 4112),     # direct loads, few tiles, long K

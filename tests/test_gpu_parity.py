@@ -289,14 +289,14 @@ def test_tile_shapes_with_tails(variant, shape):
 # (64 x 64 tiles, K a multiple of 16, 16-byte-aligned rows, every tile
 # inside the matrices, at least twice as many slices as stages, no split),
 # in both 64 x 64 tile classes, with M and N not multiples of the tile
-# (edge tiles moved inside), at the fewest slices the pipeline takes and one
-# more, and one tile alone: (M, N, K, kernel the MFMA rung plans).  The
+# (edge tiles moved inside), at the fewest slices that take it and one more,
+# and one tile alone: (M, N, K, kernel the MFMA rung plans).  The
 # stream-K form of the same shapes runs register-staged.
 DMA_SHAPES = [
     (1000, 1000, 1024, "<64x64x16, 4 waves, 4 LDS stages>"),
-    (1000, 1000, 128, "<64x64x16, 4 waves, 4 LDS stages>"),    # 8 slices: the fewest
-    (1000, 1000, 144, "<64x64x16, 4 waves, 4 LDS stages>"),    # 9: one round and a tail
-    (64, 64, 128, "<64x64x16, 4 waves, 4 LDS stages>"),        # one tile
+    (1000, 1000, 512, "<64x64x16, 4 waves, 4 LDS stages>"),    # 32 slices: the fewest
+    (1000, 1000, 528, "<64x64x16, 4 waves, 4 LDS stages>"),    # 33: a tail of 5
+    (64, 64, 560, "<64x64x16, 4 waves, 4 LDS stages>"),        # one tile, a tail of 7
     (700, 900, 1536, "<64x64x16, 4 waves, 6 LDS stages>"),
     (64, 64, 1040, "<64x64x16, 4 waves, 6 LDS stages>"),       # 65 slices, one tile
     (3000, 2052, 1536, "<64x64x16, 4 waves, 6 LDS stages>"),   # 1551 tiles
@@ -577,7 +577,7 @@ def test_random_shapes_small_ints_exact(variant):
 
 def _random_direct_load_shapes(seed, n):
     # shapes whose MFMA launch stages with direct loads: M, N >= 64, N a
-    # multiple of 4, K a multiple of 16 with at least 8 slices (4 stages,
+    # multiple of 4, K a multiple of 16 with at least 32 slices (4 stages,
     # K <= 1024) or more than 64 (6 stages); leading dimensions padded by
     # whole quads, so rows stay 16-byte aligned
     rng = np.random.default_rng(seed)
@@ -585,7 +585,7 @@ def _random_direct_load_shapes(seed, n):
     for i in range(n):
         M = int(rng.integers(64, 700))
         N = 4 * int(rng.integers(16, 175))
-        K = 16 * int(rng.integers(8, 65) if i % 2 == 0 else rng.integers(65, 100))
+        K = 16 * int(rng.integers(32, 65) if i % 2 == 0 else rng.integers(65, 100))
         pads = tuple(4 * int(x) for x in rng.integers(0, 3, size=3))
         out.append((M, N, K, pads))
     return out

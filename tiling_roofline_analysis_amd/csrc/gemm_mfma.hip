@@ -1223,10 +1223,15 @@ int64_t main_grid(const Split &r) {
 }
 
 // True when every tile lies inside the matrices with float4 rows
-// (aligned_launch) and every slice is full, with enough slices for the
-// direct-load pipeline: the main launch then stages with direct loads.
+// (aligned_launch), every slice is full and there are at least 32 slices:
+// the main launch then stages with direct loads.  (Shorter K lost to the
+// register path, most where a CU runs many short tiles: 5265 x 2016 x 240,
+// 15 slices, 7%; 4849 x 1608 x 496, 31 slices, 1%; 1024^2 x 128 1%.  From
+// 32 slices on it gained: 1024^2 x 512 +0.8 to 1.6%, 5308 x 1328 x 528
+// +0.5%, 2403 x 4156 x 880 +0.5%.)  The K loop itself needs 2 S slices.
+constexpr int64_t kDmaMinSlices = 32;
 inline bool dma_ok(bool aligned, int64_t K, int64_t bk, int64_t stages) {
-    return aligned && K % bk == 0 && K / bk >= 2 * stages;
+    return aligned && K % bk == 0 && K / bk >= kDmaMinSlices && K / bk >= 2 * stages;
 }
 
 // `name`, or `dma_name` when the main launch stages with direct loads
