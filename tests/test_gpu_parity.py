@@ -421,8 +421,11 @@ def strided_on_device(x: np.ndarray, ld: int):
 @pytest.mark.parametrize("variant", RUNGS + [tra.AUTO], ids=RUNG_IDS + ["auto"])
 def test_offsets_past_2_31_elements(variant, case):
     import torch
+    # K = 512 (32 slices) and K = 40000: the MFMA rung's unsplit launches
+    # stage these with direct loads into LDS, the split ones through
+    # registers
     if case == "A_and_C_rows":
-        M, N, K = 40000, 64, 64
+        M, N, K = 40000, 64, 512
     else:
         M, N, K = 64, 64, 40000
     A, B = int_inputs(M, N, K)
