@@ -72,14 +72,29 @@ struct RbCtx {
 };
 
 // Loads slice k0 .. k0+BK of the A and B tiles into registers, in MODE.
-template <class T, int MODE>
+// Staging slot f moves quad kq of row m of A (BK = 16: four quads a row).
+// Plain: four consecutive slots take the four quads of one row and 16
+// consecutive slots four consecutive rows, whose LDS stores (rows 20 words
+// apart) put rows a and a+3 in the same banks: 0.26 conflict cycles per LDS
+// instruction.  SPREAD: the 16 slots take rows a, a+4, a+8 and a+12 of a
+// 16-row group, which start in bank groups 5a, 5a+4, 5a+8 and 5a+12 (mod
+// 16): no conflict, and each row is still read as one 64-byte segment by
+// four consecutive lanes.  The index costs registers the 256-lane kernels
+// cannot spare (the 64x64 kernel went from 80 to 86 VGPRs, a wave less per
+// SIMD: 2048^3 7% and 3000 x 2049 x 1531 4.5% slower); the K-split kernel,
+// one workgroup a CU, takes it (1024^3 32.6 -> 30.7 us).  The same map
+// written through a helper function compiled the K-split kernel's loop
+// with other registers and gained nothing, so it is written out here.
+template <class T, int MODE, bool SPREAD>
 __device__ __forceinline__ void rb_fetch(const RbCtx &c, int64_t k0, float4 (&ra)[T::AF4],
                                          float4 (&rb)[T::BF4]) {
     constexpr int BK = T::BK, BN = T::BN;
+    static_assert(BK == 16 && T::BM % 16 == 0, "four quads a row, rows in groups of 16");
 #pragma unroll
     for (int r = 0; r < T::AF4; ++r) {
         const int f = c.t + T::THREADS * r;
-        const int m = f / (BK / 4), kq = f % (BK / 4);
+        const int m = SPREAD ? (f >> 6) * 16 + ((f >> 4) & 3) + 4 * ((f >> 2) & 3) : f / (BK / 4),
+                  kq = SPREAD ? f & 3 : f % (BK / 4);
         const float *p = c.A + (c.m0 + m) * c.lda + k0 + 4 * kq;
         if (MODE == kVec || MODE == kVecA) ra[r] = *reinterpret_cast<const float4 *>(p);
         else if (MODE == kScalar) ra[r] = load4_scalar(p);
@@ -96,14 +111,15 @@ __device__ __forceinline__ void rb_fetch(const RbCtx &c, int64_t k0, float4 (&ra
     }
 }
 
-template <class T>
+template <class T, bool SPREAD>
 __device__ __forceinline__ void rb_stage(float *as, float *bs, int t, const float4 (&ra)[T::AF4],
                                          const float4 (&rb)[T::BF4]) {
     constexpr int BK = T::BK, BN = T::BN;
 #pragma unroll
     for (int r = 0; r < T::AF4; ++r) {
         const int f = t + T::THREADS * r;
-        const int m = f / (BK / 4), kq = f % (BK / 4);
+        const int m = SPREAD ? (f >> 6) * 16 + ((f >> 4) & 3) + 4 * ((f >> 2) & 3) : f / (BK / 4),
+                  kq = SPREAD ? f & 3 : f % (BK / 4);
         *reinterpret_cast<float4 *>(&as[m * T::AST + 4 * kq]) = ra[r];
     }
 #pragma unroll
@@ -160,7 +176,7 @@ __device__ __forceinline__ void rb_compute(const float *as, const float *bs, int
 // barrier per slice.  (Without RANGE the first slice is 0 at compile time:
 // a run-time start made the compiler's code for the whole-K loop up to 55%
 // slower, at 1000^3.)
-template <class T, int MODE, bool RANGE = false>
+template <class T, int MODE, bool RANGE = false, bool SPREAD = false>
 __device__ __forceinline__ void rb_k_loop(const RbCtx &c, float *As, float *Bs, int tx, int ty,
                                           float (&acc)[T::TM][T::TN], int64_t first = 0,
                                           int64_t count = 0) {
@@ -171,16 +187,16 @@ __device__ __forceinline__ void rb_k_loop(const RbCtx &c, float *As, float *Bs, 
     const int64_t full = RANGE ? (c.K / BK - s0 < count ? c.K / BK - s0 : count) : c.K / BK;
     if (slices <= 0) return;
     float4 ra[T::AF4], rb[T::BF4];
-    if (full > 0) rb_fetch<T, MODE>(c, s0 * BK, ra, rb);
-    else rb_fetch<T, kChecked>(c, s0 * BK, ra, rb);
-    rb_stage<T>(As, Bs, c.t, ra, rb);
+    if (full > 0) rb_fetch<T, MODE, SPREAD>(c, s0 * BK, ra, rb);
+    else rb_fetch<T, kChecked, SPREAD>(c, s0 * BK, ra, rb);
+    rb_stage<T, SPREAD>(As, Bs, c.t, ra, rb);
     __syncthreads();
     int64_t s = 0;
     for (; s + 1 < full; ++s) {
         const int cur = static_cast<int>(s & 1);
-        rb_fetch<T, MODE>(c, (s0 + s + 1) * BK, ra, rb);
+        rb_fetch<T, MODE, SPREAD>(c, (s0 + s + 1) * BK, ra, rb);
         rb_compute<T>(As + cur * AW, Bs + cur * BW, tx, ty, acc);
-        rb_stage<T>(As + (cur ^ 1) * AW, Bs + (cur ^ 1) * BW, c.t, ra, rb);
+        rb_stage<T, SPREAD>(As + (cur ^ 1) * AW, Bs + (cur ^ 1) * BW, c.t, ra, rb);
         __syncthreads();
     }
     // One or two slices are left: slice s, and the slice past K if there
@@ -189,9 +205,9 @@ __device__ __forceinline__ void rb_k_loop(const RbCtx &c, float *As, float *Bs, 
     // tile's registers.)
     if (s + 1 < slices) {
         const int cur = static_cast<int>(s & 1);
-        rb_fetch<T, kChecked>(c, (s0 + s + 1) * BK, ra, rb);
+        rb_fetch<T, kChecked, SPREAD>(c, (s0 + s + 1) * BK, ra, rb);
         rb_compute<T>(As + cur * AW, Bs + cur * BW, tx, ty, acc);
-        rb_stage<T>(As + (cur ^ 1) * AW, Bs + (cur ^ 1) * BW, c.t, ra, rb);
+        rb_stage<T, SPREAD>(As + (cur ^ 1) * AW, Bs + (cur ^ 1) * BW, c.t, ra, rb);
         __syncthreads();
         ++s;
     }
@@ -321,13 +337,13 @@ void gemm_regblock_f32_ks(int64_t M, int64_t N, int64_t K,
     float *Bs = As + 2 * BM * T::AST;
     const bool inside = o.m0 + BM <= M && o.n0 + BN <= N;
     if (!inside)
-        rb_k_loop<T, kChecked, true>(c, As, Bs, tx, ty, acc, g * per, per);
+        rb_k_loop<T, kChecked, true, true>(c, As, Bs, tx, ty, acc, g * per, per);
     else if (vec_a && vec_b && (o.n0 & 3) == 0)
-        rb_k_loop<T, kVec, true>(c, As, Bs, tx, ty, acc, g * per, per);
+        rb_k_loop<T, kVec, true, true>(c, As, Bs, tx, ty, acc, g * per, per);
     else if (vec_a)
-        rb_k_loop<T, kVecA, true>(c, As, Bs, tx, ty, acc, g * per, per);
+        rb_k_loop<T, kVecA, true, true>(c, As, Bs, tx, ty, acc, g * per, per);
     else
-        rb_k_loop<T, kScalar, true>(c, As, Bs, tx, ty, acc, g * per, per);
+        rb_k_loop<T, kScalar, true, true>(c, As, Bs, tx, ty, acc, g * per, per);
 
     // the partial tiles, row-major with rows of PST words, then each lane
     // adds one float4 of the tile over the groups and stores it
