@@ -122,6 +122,10 @@ def test_direct_load_loops_keep_loads_in_flight(asm):
     for name, body in funcs.items():
         code = "\n".join(line.split(";")[0] for line in body.splitlines())
         assert "global_load_lds_dwordx4" in code, name
+        # every direct load writes LDS at the address in M0, so the kernel
+        # sets M0 (a compiler of this family has been seen to drop that for
+        # a direct load into an LDS array at a constant address)
+        assert re.search(r"^\s+s_\w+\s+m0,", code, re.M), f"{name}: M0 never set"
         main = [lp for lp in _loops(body) if "global_load_lds_dwordx4" in lp
                 and "v_mfma_f32_32x32x2_f32" in lp]
         assert main, f"{name}: no loop with direct loads and MFMAs"
