@@ -75,12 +75,15 @@ def test_describe_plans():
     d = tra.tra_gemm_describe(tra.MFMA, 16384, 64, 16384)
     assert "tile=64x64x16" in d and "6 LDS stages" in d and "grid=256" in d
     assert "lds_bytes=50688" in d
-    # K not a multiple of 16: register-staged slices, two LDS buffers
+    # K not a multiple of 4: register-staged slices, two LDS buffers
     d = tra.tra_gemm_describe(tra.MFMA, 3000, 2049, 1531)
     assert "tile=64x64x16" in d and "4 sets" in d and "grid=1551" in d and "block=256" in d
     assert "lds_bytes=18944" in d
-    d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 1000)
+    d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 1002)
     assert "<64x64x16, 4 waves>" in d and "lds_bytes=18944" in d
+    # K a multiple of 4 but not of 16: direct loads, the last slice checked
+    d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 1000)
+    assert "4 LDS stages" in d and "lds_bytes=33792" in d
     # fewer than 32 slices: register-staged
     d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 496)
     assert "<64x64x16, 4 waves>" in d
@@ -341,7 +344,7 @@ def test_auto_choice(shape, rung):
     ((2048, 2048, 2048), "<128x128x16, 8 waves>"),          # one 128x128 tile a CU
     ((2304, 2304, 2304), "<128x128x16, 8 waves>"),          # 324 tiles, long K: parts
     ((2000, 2600, 3000), "<128x128x16, 8 waves>"),          # 336 tiles, edges wasted no worse
-    ((3000, 3000, 1000), "<64x64x16, 4 waves>"),            # short K stays on 64x64
+    ((3000, 3000, 1000), "<64x64x16, 4 waves, 4 LDS stages>"),     # short K stays on 64x64
     ((3072, 3072, 3072), "<64x64x16, 4 waves, 6 LDS stages>"),     # 576 tiles: 2.25 a CU
 ])
 def test_auto_tile_class(shape, tile):
@@ -377,8 +380,11 @@ def test_split_plans_hold_their_invariants():
         elif form == "parts":
             parts = wgs // sk
             assert wgs == sk * parts and 2 <= parts <= 8 and 2 * parts <= ipt
-            wave = 256 * (1 if block == 512 else (4 if "4 sets" not in
-                                                  tra.tra_gemm_describe(tra.MFMA, M, N, K) else 3))
+            # the deep 64 x 64 tile (4 register sets, or 6 LDS stages when it
+            # loads directly) is planned at three workgroups a CU
+            plain = tra.tra_gemm_describe(tra.MFMA, M, N, K)
+            deep = "4 sets" in plain or "6 LDS stages" in plain
+            wave = 256 * (1 if block == 512 else (3 if deep else 4))
             assert sk == tiles % wave and wgs <= wave
             assert grid == tiles + sk * (parts - 1) and ws == wgs * bm * bn * 4
         else:

@@ -45,6 +45,8 @@ SHAPES = [
     (700, 900, 1536),     # direct loads, 64 x 64, 6 stages
     (64, 64, 1040),       # direct loads, one tile
     (200, 300, 4112),     # direct loads, few tiles, long K
+    (1000, 1000, 1000),   # direct loads, the last slice past K
+    (700, 900, 1548),     # direct loads, 6 stages, the last slice past K
 ]
 
 

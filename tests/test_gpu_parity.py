@@ -249,14 +249,16 @@ def test_edge_sizes_all_pairs(variant):
 
 
 # Shapes that send the MFMA rung to each of its tile shapes, with tails on
-# every axis: (M, N, K, expected tile).
+# every axis and register-staged slices (K not a multiple of 4 where the
+# 64 x 64 tiles would otherwise load directly into LDS): (M, N, K, expected
+# tile).
 MFMA_TILE_SHAPES = [
     (4000, 4200, 203, "<256x128x16, 8 waves, 4 sets>"),   # 16 x 33 = 528 tiles of 256 x 128
     (1900, 2000, 300, "<128x128x16, 8 waves>"),   # 15 x 16 = 240 tiles of 128 x 128
     (1500, 1500, 77, "<64x64x16, 4 waves>"),      # 576 tiles of 64 x 64, short K
-    (200, 300, 4100, "<64x64x16, 4 waves, 4 sets>"),   # few tiles, long K
+    (200, 300, 4101, "<64x64x16, 4 waves, 4 sets>"),   # few tiles, long K
     (300, 500, 203, "<64x64x16, 4 waves>"),       # few tiles
-    (700, 900, 1500, "<64x64x16, 4 waves, 4 sets>"),   # 165 tiles, K > 1024
+    (700, 900, 1501, "<64x64x16, 4 waves, 4 sets>"),   # 165 tiles, K > 1024
     (2040, 4090, 300, "<256x128x16, 8 waves, 4 sets>"),   # 8 x 32 = 256 tiles of 256 x 128
     (2000, 2600, 2050, "<128x128x16, 8 waves>"),  # 336 tiles of 128 x 128, K >= 2048
     (3000, 32, 1100, "<64x64x16, 4 waves, 4 sets>"),   # narrower than a tile (float4 loads)
@@ -301,6 +303,11 @@ DMA_SHAPES = [
     (64, 64, 1040, "<64x64x16, 4 waves, 6 LDS stages>"),       # 65 slices, one tile
     (3000, 2052, 1536, "<64x64x16, 4 waves, 6 LDS stages>"),   # 1551 tiles
     (200, 300, 4112, "<64x64x16, 4 waves, 6 LDS stages>"),     # 20 tiles, long K
+    # K a multiple of 4 but not of 16: the last slice runs past K
+    (1000, 1000, 1000, "<64x64x16, 4 waves, 4 LDS stages>"),   # 8 of its 16 k inside
+    (1000, 1000, 516, "<64x64x16, 4 waves, 4 LDS stages>"),    # 4 inside, 33 slices
+    (700, 900, 1548, "<64x64x16, 4 waves, 6 LDS stages>"),     # 12 inside
+    (64, 64, 1044, "<64x64x16, 4 waves, 6 LDS stages>"),       # one tile, 4 inside
 ]
 
 
@@ -580,8 +587,9 @@ def test_random_shapes_small_ints_exact(variant):
 
 def _random_direct_load_shapes(seed, n):
     # shapes whose MFMA launch stages with direct loads: M, N >= 64, N a
-    # multiple of 4, K a multiple of 16 with at least 32 slices (4 stages,
-    # K <= 1024) or more than 64 (6 stages); leading dimensions padded by
+    # multiple of 4, K with at least 32 slices (4 stages, K <= 1024) or more
+    # than 64 (6 stages), a multiple of 16 or only of 4 (the last slice
+    # running past K); leading dimensions padded by
     # whole quads, so rows stay 16-byte aligned
     rng = np.random.default_rng(seed)
     out = []
@@ -589,6 +597,8 @@ def _random_direct_load_shapes(seed, n):
         M = int(rng.integers(64, 700))
         N = 4 * int(rng.integers(16, 175))
         K = 16 * int(rng.integers(32, 65) if i % 2 == 0 else rng.integers(65, 100))
+        if i % 4 >= 2:
+            K -= 4 * int(rng.integers(1, 4))   # the last slice runs past K
         pads = tuple(4 * int(x) for x in rng.integers(0, 3, size=3))
         out.append((M, N, K, pads))
     return out

@@ -117,8 +117,9 @@ def test_direct_load_loops_keep_loads_in_flight(asm):
     # an earlier direct load, and it would serialise the pipeline.
     funcs = {n: b for n, b in _functions(asm["gemm_mfma.hip"]).items()
              if n.startswith("_ZN3tra12_GLOBAL__N_113gemm_mfma_f32INS0_8MfmaTile")
-             and n.endswith("Lb1ELb1EEEvlllPKflS5_lPflNS0_6SkPlanEiii")}
-    assert len(funcs) == 2, sorted(funcs)   # the two 64 x 64 tiles
+             and re.search(r"Lb1ELi[12]EEEvlllPKflS5_lPflNS0_6SkPlanEiii$", n)}
+    # the two 64 x 64 tiles, with full slices and with a slice past K
+    assert len(funcs) == 4, sorted(funcs)
     for name, body in funcs.items():
         code = "\n".join(line.split(";")[0] for line in body.splitlines())
         assert "global_load_lds_dwordx4" in code, name

@@ -478,6 +478,12 @@ __device__ __forceinline__ void dma_sync() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// One direct load: 16 bytes per lane from src to LDS at dst + 16 lane
+// (dst is the wave's base, the same for every lane).
+__device__ __forceinline__ void dma16(const float *src, float *dst) {
+    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
 template <class T>
 struct DmaLane {
     const float *pa[Dma<T>::A_INS];   // this lane's A quad of slice 0, per instruction
@@ -518,12 +524,33 @@ __device__ __forceinline__ void dma_issue(const DmaLane<T> &d, float *stage, int
     using D = Dma<T>;
 #pragma unroll
     for (int i = 0; i < D::A_INS; ++i)
-        __builtin_amdgcn_global_load_lds(d.pa[i] + k0, stage + d.wa + i * T::WAVES * 256, 16, 0,
-                                         0);
+        dma16(d.pa[i] + k0, stage + d.wa + i * T::WAVES * 256);
 #pragma unroll
     for (int i = 0; i < D::B_INS; ++i)
-        __builtin_amdgcn_global_load_lds(d.pb[i] + k0 * ldb,
-                                         stage + d.wb + i * T::WAVES * D::B_BLOCK, 16, 0, 0);
+        dma16(d.pb[i] + k0 * ldb, stage + d.wb + i * T::WAVES * D::B_BLOCK);
+}
+
+// The same loads for the slice that runs past K (K a multiple of 4, so a
+// quad of A along k lies wholly inside or outside): a quad of A past K, or
+// a row of B past K, loads the 16-byte zero word instead.
+template <class T>
+__device__ __forceinline__ void dma_issue_tail(const DmaLane<T> &d, float *stage, int64_t k0,
+                                               int64_t K, int64_t ldb, int t) {
+    using D = Dma<T>;
+    const int lane = t & 63, wave = t >> 6;
+#pragma unroll
+    for (int i = 0; i < D::A_INS; ++i) {
+        const int g = (i * T::WAVES + wave) * 64 + lane;
+        const int m = g >> 2, q = (g & 3) ^ ((m >> 2) & 3);
+        dma16(k0 + 4 * q < K ? d.pa[i] + k0 : &g_zero4[0], stage + d.wa + i * T::WAVES * 256);
+    }
+#pragma unroll
+    for (int i = 0; i < D::B_INS; ++i) {
+        const int g = (i * T::WAVES + wave) * 64 + lane;
+        const int k = g / (T::BN / 4);
+        dma16(k0 + k < K ? d.pb[i] + k0 * ldb : &g_zero4[0],
+              stage + d.wb + i * T::WAVES * D::B_BLOCK);
+    }
 }
 
 // A lane's fragments of the slice in a stage: A rows arow + 32 i, k quads
@@ -577,11 +604,12 @@ __device__ __forceinline__ void dma_order() {
     dma_schedule<0, NM, (NDR + FIRST - 1) / FIRST, (Dma<T>::NV + SECOND - 1) / SECOND>();
 }
 
-// The K loop over the n slices of a tile when every slice is full and
-// every load is an aligned float4 inside the matrices (K a multiple of BK,
-// A and B rows 16-byte aligned, the tile inside), n >= 2 S.  stg: the S
+// The K loop over the n slices of a tile when every load is an aligned
+// float4 inside the matrices (A and B rows 16-byte aligned, the tile
+// inside) and every slice is full -- or, with TAIL, every slice but the
+// last, which runs past K (K a multiple of 4); n >= 2 S + 1.  stg: the S
 // stage arrays.
-template <class T>
+template <class T, bool TAIL>
 __device__ __forceinline__ void k_loop_dma(const Ctx<T> &c, float *const *stg, int arow,
                                            int bcol, int kbase, f32x16 (&acc)[T::FM][T::FN],
                                            int64_t n) {
@@ -598,7 +626,10 @@ __device__ __forceinline__ void k_loop_dma(const Ctx<T> &c, float *const *stg, i
     dma_frags<T>(d, stg[0], kbase, fr[0]);
     dma_sync<(S - 2) * D::NV>();
     int64_t s = 0;
-    for (; s + S - 1 + S < n; s += S) {
+    // with TAIL the last slice is left to the loop below, which checks it
+    int64_t loads = n;
+    if constexpr (TAIL) loads = n - 1;
+    for (; s + S - 1 + S < loads; s += S) {
 #pragma unroll
         for (int u = 0; u < S; ++u) {
             __builtin_amdgcn_sched_barrier(0);
@@ -624,7 +655,14 @@ __device__ __forceinline__ void k_loop_dma(const Ctx<T> &c, float *const *stg, i
                 __builtin_amdgcn_sched_barrier(0);
                 mfmas<T, 0, T::HALF>(fr[u & 1], acc);
                 const int64_t next = s + u + S < n ? s + u + S : n - 1;
-                dma_issue<T>(d, stg[u], next * BK, c.ldb);
+                if constexpr (TAIL) {
+                    if (next == n - 1)
+                        dma_issue_tail<T>(d, stg[u], next * BK, c.K, c.ldb, c.t);
+                    else
+                        dma_issue<T>(d, stg[u], next * BK, c.ldb);
+                } else {
+                    dma_issue<T>(d, stg[u], next * BK, c.ldb);
+                }
                 dma_sync<(S - 2) * D::NV>();
             }
         }
@@ -695,9 +733,10 @@ __host__ __device__ __forceinline__ int64_t part_begin(const PartPlan &p, int j)
 // One pass of the block tile at (c.m0, c.n0) over slices s0 .. s0+n-1
 // (n = 0: a zero tile).  Stores rows [row_lo, rows) and columns
 // [col_lo, cols) of the tile to `out` (its corner, leading dimension ldo).
-// DMA: the host found every slice full with aligned float4 rows inside the
-// matrices (dma_launch); stg then holds the direct-load stages.
-template <class T, bool ALIGNED = false, bool DMA = false>
+// DMA (dma_mode): 1 when the host found every slice full with aligned
+// float4 rows inside the matrices, 2 when the same holds but the last slice
+// runs past K (K a multiple of 4); stg then holds the direct-load stages.
+template <class T, bool ALIGNED = false, int DMA = 0>
 __device__ __forceinline__ void tile_pass(const Ctx<T> &c, int vec_a, int vec_b, float *lds,
                                           int64_t s0, int64_t n, float *out, int64_t ldo,
                                           int row_lo, int64_t rows, int col_lo, int64_t cols,
@@ -720,8 +759,10 @@ __device__ __forceinline__ void tile_pass(const Ctx<T> &c, int vec_a, int vec_b,
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    if (DMA) {
-        k_loop_dma<T>(c, stg, wm0 + l32, wn0 + l32, kbase, acc, n);
+    if constexpr (DMA == 1) {
+        k_loop_dma<T, false>(c, stg, wm0 + l32, wn0 + l32, kbase, acc, n);
+    } else if constexpr (DMA == 2) {
+        k_loop_dma<T, true>(c, stg, wm0 + l32, wn0 + l32, kbase, acc, n);
     } else if (ALIGNED && n > 0) {
         // the host found every tile inside the matrices with float4 rows
         k_loop<T, kVec>(c, lds, wm0 + l32, wn0 + l32, kbase, acc, s0, n);
@@ -874,10 +915,10 @@ __device__ __forceinline__ void part_fixup(int job, int64_t M, int64_t N, float 
 // aligned_launch), so the kernel holds that load mode's K loop alone --
 // a third of the code, whose first fetch into the instruction cache of
 // every CU is part of each launch's fixed cost (1024^3: 19.59 -> 19.44 us).
-// DMA: in addition every slice is full (dma_launch), and the K loop stages
-// the slices with direct loads (k_loop_dma) in S stage arrays instead of
-// the two register-staged buffers.
-template <class T, bool ALIGNED, bool DMA = false>
+// DMA (dma_mode, 1 or 2): in addition the slices are full, or all but the
+// last, and the K loop stages them with direct loads (k_loop_dma) in S
+// stage arrays instead of the two register-staged buffers.
+template <class T, bool ALIGNED, int DMA = 0>
 __global__ __launch_bounds__(T::THREADS)
 void gemm_mfma_f32(int64_t M, int64_t N, int64_t K,
                    const float *__restrict__ A, int64_t lda,
@@ -1222,16 +1263,22 @@ int64_t main_grid(const Split &r) {
            static_cast<int64_t>(r.sk.sk_tiles) * (extra - 1);
 }
 
-// True when every tile lies inside the matrices with float4 rows
-// (aligned_launch), every slice is full and there are at least 32 slices:
-// the main launch then stages with direct loads.  (Shorter K lost to the
-// register path, most where a CU runs many short tiles: 5265 x 2016 x 240,
-// 15 slices, 7%; 4849 x 1608 x 496, 31 slices, 1%; 1024^2 x 128 1%.  From
-// 32 slices on it gained: 1024^2 x 512 +0.8 to 1.6%, 5308 x 1328 x 528
-// +0.5%, 2403 x 4156 x 880 +0.5%.)  The K loop itself needs 2 S slices.
+// How the main launch stages its slices: 0 through registers; with direct
+// loads when every tile lies inside the matrices with float4 rows
+// (aligned_launch) and there are at least 32 slices -- 1 when every slice
+// is full, 2 when the last one runs past K and K is a multiple of 4 (so a
+// quad of A along k is wholly inside or outside the matrix).  (Shorter K
+// lost to the register path, most where a CU runs many short tiles:
+// 5265 x 2016 x 240, 15 slices, 7%; 4849 x 1608 x 496, 31 slices, 1%;
+// 1024^2 x 128 1%.  From 32 slices on it gained: 1024^2 x 512 +0.8 to
+// 1.6%, 5308 x 1328 x 528 +0.5%, 2403 x 4156 x 880 +0.5%.)  The K loop
+// itself needs 2 S + 1 slices.
 constexpr int64_t kDmaMinSlices = 32;
-inline bool dma_ok(bool aligned, int64_t K, int64_t bk, int64_t stages) {
-    return aligned && K % bk == 0 && K / bk >= kDmaMinSlices && K / bk >= 2 * stages;
+inline int dma_mode(bool aligned, int64_t K, int64_t bk, int64_t stages) {
+    const int64_t n = ceil_div(K, bk);
+    if (!aligned || n < kDmaMinSlices || n < 2 * stages + 1) return 0;
+    if (K % bk == 0) return 1;
+    return K % 4 == 0 ? 2 : 0;
 }
 
 // `name`, or `dma_name` when the main launch stages with direct loads
@@ -1242,7 +1289,7 @@ LaunchPlan plan_for(int64_t M, int64_t N, int64_t K, bool stream_k, const char *
                     const char *dma_name) {
     const Split r = plan_split<T>(M, N, K, stream_k);
     const bool aligned = (K & 3) == 0 && M >= T::BM && N >= T::BN && (N & 3) == 0;
-    const bool dma = Dma<T>::USED && r.sk.sk_tiles == 0 && dma_ok(aligned, K, T::BK, Dma<T>::S);
+    const bool dma = Dma<T>::USED && r.sk.sk_tiles == 0 && dma_mode(aligned, K, T::BK, Dma<T>::S);
     LaunchPlan p{};
     p.kernel = dma ? dma_name : name;
     p.bm = T::BM;
@@ -1307,12 +1354,16 @@ hipError_t launch_tile(const GemmArgs &a, bool stream_k, void *ws, size_t ws_byt
     // (2560^3 with stream-K runs: 256 -> 402 us with direct loads)
     const bool aligned = aligned_launch<T>(a, vec_a, vec_b);
     if constexpr (Dma<T>::USED) {
-        if (p.sk_tiles == 0 && dma_ok(aligned, a.K, T::BK, Dma<T>::S)) {
-            hipLaunchKernelGGL((gemm_mfma_f32<T, true, true>), grid, dim3(T::THREADS), 0,
-                               a.stream, a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, p,
-                               vec_a, vec_b, vec_c);
-            return hipGetLastError();
-        }
+        const int mode = p.sk_tiles == 0 ? dma_mode(aligned, a.K, T::BK, Dma<T>::S) : 0;
+        if (mode == 1)
+            hipLaunchKernelGGL((gemm_mfma_f32<T, true, 1>), grid, dim3(T::THREADS), 0, a.stream,
+                               a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, p, vec_a,
+                               vec_b, vec_c);
+        else if (mode == 2)
+            hipLaunchKernelGGL((gemm_mfma_f32<T, true, 2>), grid, dim3(T::THREADS), 0, a.stream,
+                               a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, p, vec_a,
+                               vec_b, vec_c);
+        if (mode != 0) return hipGetLastError();
     }
     if (aligned)
         hipLaunchKernelGGL((gemm_mfma_f32<T, true>), grid, dim3(T::THREADS), 0, a.stream, a.M,
