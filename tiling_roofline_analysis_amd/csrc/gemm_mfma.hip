@@ -42,12 +42,13 @@
 // iteration overlaps that iteration's MFMAs; the memory instructions are
 // issued between the MFMAs (il_order) rather than in bursts.
 //
-// Direct staging (k_loop_dma): where every slice is full and every load an
-// aligned float4 inside the matrices -- the common case of contiguous
-// operands with K a multiple of 16 -- the slices go from global memory
+// Direct staging (k_loop_dma): where every load is an aligned float4 inside
+// the matrices and K is a multiple of 4 -- the common case of contiguous
+// operands -- the 64 x 64 tiles move their slices from global memory
 // straight into a ring of S LDS stages (global_load_lds_dwordx4), with no
-// register sets and no LDS stores; the layout and the waits are described
-// at Dma below.
+// register sets and no LDS stores; the slice that runs past K, if any,
+// reads a zero word for the quads past K.  The layout and the waits are
+// described at Dma below.
 //
 // Global loads: a tile that would cross row M or column N is moved back
 // inside the matrices (its rows and columns shared with the neighbouring
