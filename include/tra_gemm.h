@@ -80,16 +80,23 @@ typedef enum tra_status {
  *                memory (page "GEMM kernel test code & optimization
  *                (1024^3 experiment)", section "How the naive GEMM kernel
  *                works").
- *   LDS_TILED    32x32 tiles of A and B staged in LDS, each lane one element
- *                of C, zero-filled outside the matrices (same page, section
+ *   LDS_TILED    16x16 tiles of C, slices of A and B 64 deep staged in
+ *                LDS, each lane one element of C, zero-filled outside the
+ *                matrices (same page, sections "Tile concept" and
  *                "Shared-memory tiled GEMM"; page "[AutoMine++] #2 matmul
  *                trial and error", section "Breaking the memory bottleneck:
  *                Tiling").
- *   REGBLOCK_DB  128x128 block tile, 8x8 register micro-tile per lane,
- *                double-buffered LDS with register prefetch (VALU FMA).
+ *   REGBLOCK_DB  128x128 block tile with an 8x8 register micro-tile per
+ *                lane (64x64 with 4x4 when the large tiles are too few),
+ *                double-buffered LDS with register prefetch (VALU FMA);
+ *                with no more 64x64 tiles than CUs, each tile's workgroup
+ *                splits K over 2-4 lane groups.
  *   MFMA         CDNA matrix-core kernel on binary32 inputs
- *                (v_mfma_f32_32x32x2_f32), double-buffered LDS, tile shape
- *                chosen from the problem shape; one tile per workgroup.
+ *                (v_mfma_f32_32x32x2_f32), tile shape chosen from the
+ *                problem shape, one tile per workgroup; slices staged
+ *                through registers into two LDS buffers, or, on the 64x64
+ *                tiles when rows are 16-byte aligned and K is a multiple of
+ *                4, loaded straight into a ring of LDS stages.
  *   MFMA_STREAMK the MFMA kernel with the tile count decoupled from the
  *                workgroup count.  When the tiles do not fill whole waves
  *                of resident workgroups (the tile-size versus occupancy
