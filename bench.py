@@ -124,6 +124,10 @@ def measure_roofs(tra, torch):
     t = timed(lambda: tra.tra_probe_fma_f32(it, sink.data_ptr(), h), 3)
     out["valu_fp32_tflops"] = round(tra.tra_probe_work(tra.PROBE_FMA, it) / t / 1e12, 2)
     out["ridge_flop_per_byte"] = round(out["mfma_fp32_tflops"] / out["hbm_copy_tbps"], 2)
+    # the floor under a one-launch GEMM: back-to-back launches of an empty
+    # kernel on as many workgroups as the 1024^3 GEMM launches
+    t = timed(lambda: tra.tra_probe_launch(256, h), 500)
+    out["launch_floor_us"] = round(t * 1e6, 2)
     return out
 
 

@@ -260,6 +260,11 @@ TRA_API tra_status tra_gemm_describe(int variant, int64_t M, int64_t N, int64_t 
  *                       (v_mfma_f32_32x32x2_f32) from registers.
  *   tra_probe_fma_f32   the same grid, each lane `iters` rounds of 8
  *                       independent v_fma_f32.
+ *   tra_probe_launch    `workgroups` workgroups of 256 lanes that do
+ *                       nothing (1 <= workgroups, workgroups x 256 <=
+ *                       2^32 - 1, else TRA_ERR_INVALID_ARG): timed back to
+ *                       back, the cost of a launch that does no work -- the
+ *                       floor under any one-launch GEMM's time.
  * The compute probes write TRA_PROBE_SINK_FLOATS floats of no meaning to
  * `sink` (device memory owned by the caller).
  */
@@ -276,6 +281,7 @@ TRA_API double tra_probe_work(int probe, int64_t amount);
 TRA_API tra_status tra_probe_copy_f32(int64_t n, const float *src, float *dst, void *stream);
 TRA_API tra_status tra_probe_mfma_f32(int64_t iters, float *sink, void *stream);
 TRA_API tra_status tra_probe_fma_f32(int64_t iters, float *sink, void *stream);
+TRA_API tra_status tra_probe_launch(int64_t workgroups, void *stream);
 
 /*
  * tra_gemm_release_workspaces: frees every workspace that gemm_f32 and

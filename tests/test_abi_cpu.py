@@ -227,6 +227,9 @@ def test_probe_invalid_arguments_rejected_on_host():
     assert tra.tra_probe_copy_f32(16, A_ADDR + 4, B_ADDR, None) == bad     # misaligned
     assert tra.tra_probe_copy_f32(16, A_ADDR, A_ADDR + 32, None) == bad    # overlap
     assert tra.tra_probe_copy_f32(0, None, None, None) == tra.TRA_OK
+    assert tra.tra_probe_launch(0, None) == bad
+    assert tra.tra_probe_launch(-3, None) == bad
+    assert tra.tra_probe_launch(1 << 24, None) == bad      # 2^32 lanes, one too many
     assert tra.tra_probe_mfma_f32(-1, C_ADDR, None) == bad
     assert tra.tra_probe_mfma_f32(1, None, None) == bad
     assert tra.tra_probe_fma_f32(-1, C_ADDR, None) == bad

@@ -41,6 +41,13 @@ def test_compute_probes_run():
     assert torch.isfinite(sink).all()
 
 
+def test_launch_probe_runs():
+    import torch
+    for wgs in (1, 256, 4096):
+        assert tra.tra_probe_launch(wgs, None) == tra.TRA_OK
+    torch.cuda.synchronize()
+
+
 def test_measured_roofs_plausible():
     import torch
     import bench
@@ -48,3 +55,4 @@ def test_measured_roofs_plausible():
     assert 2.0 < r["hbm_copy_tbps"] < 9.0
     assert 60.0 < r["mfma_fp32_tflops"] < 170.0
     assert 20.0 < r["valu_fp32_tflops"] < 170.0
+    assert 0.5 < r["launch_floor_us"] < 50.0

@@ -49,7 +49,8 @@ ABI_FUNCTIONS = ("gemm_f32", "gemm_f32_variant", "gemm_f32_variant_ws",
                  "tra_gemm_workspace_size", "tra_gemm_release_workspaces",
                  "tra_gemm_describe", "tra_status_string",
                  "tra_gemm_variant_name", "tra_last_hip_error", "tra_probe_work",
-                 "tra_probe_copy_f32", "tra_probe_mfma_f32", "tra_probe_fma_f32")
+                 "tra_probe_copy_f32", "tra_probe_mfma_f32", "tra_probe_fma_f32",
+                 "tra_probe_launch")
 
 # tra_probe
 PROBE_COPY = 0
@@ -135,6 +136,8 @@ def _open(path: str) -> ctypes.CDLL:
     lib.tra_probe_mfma_f32.restype = c_int
     lib.tra_probe_fma_f32.argtypes = [i64, p, p]
     lib.tra_probe_fma_f32.restype = c_int
+    lib.tra_probe_launch.argtypes = [i64, p]
+    lib.tra_probe_launch.restype = c_int
     return lib
 
 
@@ -204,6 +207,10 @@ def tra_probe_mfma_f32(iters, sink, stream=None) -> int:
 
 def tra_probe_fma_f32(iters, sink, stream=None) -> int:
     return load().tra_probe_fma_f32(iters, sink, stream)
+
+
+def tra_probe_launch(workgroups, stream=None) -> int:
+    return load().tra_probe_launch(workgroups, stream)
 
 
 # --- torch convenience --------------------------------------------------------

@@ -11,7 +11,9 @@
 //   * mfma  -- back-to-back independent v_mfma_f32_32x32x2_f32 from
 //              registers: the FP32 matrix-core roof;
 //   * fma   -- independent v_fma_f32 chains from registers: the FP32 VALU
-//              roof of code compiled without packed-FP32 instructions.
+//              roof of code compiled without packed-FP32 instructions;
+//   * launch -- an empty kernel: what a launch costs when it does no work,
+//              the floor under the time of any one-launch GEMM.
 // Each compute probe writes one value per lane to a sink so nothing is
 // optimised away; results are meaningless numbers.
 #include <algorithm>
@@ -85,6 +87,15 @@ void probe_fma_f32(int64_t iters, float *__restrict__ sink) {
     sink[static_cast<int64_t>(blockIdx.x) * kProbeThreads + threadIdx.x] = s;
 }
 
+// No work: the time of back-to-back launches of this kernel is the launch
+// floor (command processing, the cache operations between dependent
+// launches, dispatch and completion).  `never` is nonzero at run time, so
+// the store is never made; it keeps the kernel from being an empty body.
+__global__ __launch_bounds__(kProbeThreads)
+void probe_launch(int never, float *__restrict__ sink) {
+    if (never == 0 && threadIdx.x == 0) sink[blockIdx.x] = 0.0f;
+}
+
 constexpr int64_t kCopyBlocks = 1024;
 
 tra_status finish(hipError_t err) {
@@ -137,6 +148,15 @@ tra_status tra_probe_copy_f32(int64_t n, const float *src, float *dst, void *str
         return tra::finish(hipGetLastError());
     }
     return TRA_OK;
+}
+
+tra_status tra_probe_launch(int64_t workgroups, void *stream) {
+    if (workgroups < 1 || workgroups * tra::kProbeThreads > tra::kMaxGridLanes)
+        return TRA_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(tra::probe_launch, dim3(static_cast<uint32_t>(workgroups)),
+                       dim3(tra::kProbeThreads), 0, static_cast<hipStream_t>(stream), 1,
+                       static_cast<float *>(nullptr));
+    return tra::finish(hipGetLastError());
 }
 
 tra_status tra_probe_mfma_f32(int64_t iters, float *sink, void *stream) {
