@@ -1348,11 +1348,12 @@ hipError_t launch_tile(const GemmArgs &a, bool stream_k, void *ws, size_t ws_byt
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     // fixups of the stream-K tiles, then the data-parallel tiles.  Direct
-    // loads only without a split: their stage ring changes how many
-    // workgroups a CU holds (two 128 x 128 tiles where the register-staged
-    // kernel's registers allow one, two 64 x 64 deep tiles where they allow
-    // three), and the stream-K plan counts on the register-staged kernel's
-    // (2560^3 with stream-K runs: 256 -> 402 us with direct loads)
+    // loads only without a split: the splits' plans were fitted to the
+    // register-staged kernel, and a stage ring that changes how many
+    // workgroups a CU holds breaks them (2560^3, 128 x 128 tiles with
+    // stream-K runs, went from 256 to 402 us when direct loads let two
+    // workgroups share a CU; the 64 x 64 rings now hold as many as the
+    // register-staged kernels, four and three)
     const bool aligned = aligned_launch<T>(a, vec_a, vec_b);
     if constexpr (Dma<T>::USED) {
         const int mode = p.sk_tiles == 0 ? dma_mode(aligned, a.K, T::BK, Dma<T>::S) : 0;
