@@ -275,10 +275,10 @@ def test_per_thread_default_stream_keeps_one_workspace_per_thread():
 
 def test_graph_capture_takes_the_caller_workspace():
     # while a stream is captured, the library's own scratch is refused (it
-    # would be allocated into the graph); the caller's workspace and the
-    # entry point that allocates nothing are captured, and every replay --
-    # with eager work and synchronisation in between -- equals the eager
-    # result
+    # would be allocated into the graph); the caller's workspace, the entry
+    # point that allocates nothing and an unsplit direct-load launch are
+    # captured, and every replay -- with eager work and synchronisation in
+    # between -- equals the eager result
     import torch
     M, N, K = 3000, 2049, 1531
     A, B = dev(inputs.uniform(M, K, 7)), dev(inputs.uniform(K, N, 8))
@@ -295,6 +295,12 @@ def test_graph_capture_takes_the_caller_workspace():
     torch.cuda.synchronize()
     assert torch.equal(C2, eager)
     other = torch.empty((M, N), device="cuda:0")
+    # and an unsplit launch that stages its slices with direct loads into LDS
+    Md = Nd = Kd = 1024
+    Ad, Bd = dev(inputs.uniform(Md, Kd, 9)), dev(inputs.uniform(Kd, Nd, 10))
+    assert "LDS stages" in tra.tra_gemm_describe(tra.MFMA, Md, Nd, Kd)
+    eager_d = tra.matmul(Ad, Bd, variant=tra.MFMA).clone()
+    Cd = torch.full((Md, Nd), float("nan"), device="cuda:0")
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     torch.cuda.synchronize()
@@ -306,14 +312,18 @@ def test_graph_capture_takes_the_caller_workspace():
                                      C.data_ptr(), N, ws.data_ptr(), need, s.cuda_stream)
         st2 = tra.gemm_f32_variant_noalloc(tra.MFMA_STREAMK, M, N, K, A.data_ptr(), K,
                                            B.data_ptr(), N, C2.data_ptr(), N, s.cuda_stream)
+        st3 = tra.gemm_f32_variant(tra.MFMA, Md, Nd, Kd, Ad.data_ptr(), Kd, Bd.data_ptr(), Nd,
+                                   Cd.data_ptr(), Nd, s.cuda_stream)
     assert refused == tra.TRA_ERR_UNSUPPORTED
-    assert st == tra.TRA_OK and st2 == tra.TRA_OK
+    assert st == tra.TRA_OK and st2 == tra.TRA_OK and st3 == tra.TRA_OK
     for r in range(3):
         C.fill_(float("nan"))
         C2.fill_(float("nan"))
+        Cd.fill_(float("nan"))
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(C, eager), r
         assert torch.equal(C2, eager), r
+        assert torch.equal(Cd, eager_d), r
         tra.matmul(A, B, other)   # eager work between replays (library workspace)
         torch.cuda.synchronize()
