@@ -109,6 +109,42 @@ def _loops(body: str):
     return loops
 
 
+def _whole_functions(text: str):
+    """name -> assembly of every kernel function, up to its end label."""
+    return {m.group(1): m.group(2) for m in
+            re.finditer(r"^(_Z\S+):\s*;\s*@\1\n(.*?)^\.Lfunc_end", text, re.M | re.S)}
+
+
+def _direct_load_kernels(text: str):
+    return {n: b for n, b in _whole_functions(text).items()
+            if n.startswith("_ZN3tra12_GLOBAL__N_113gemm_mfma_f32INS0_8MfmaTile")
+            and re.search(r"Lb1ELi[12]EEEvlllPKflS5_lPflNS0_6SkPlanEiii$", n)}
+
+
+def test_direct_load_fragment_reads_wait_only_at_barriers(asm):
+    # Every wait for direct loads in these kernels is an explicit
+    # s_waitcnt vmcnt(n) lgkmcnt(0) followed by s_barrier.  A vector-memory
+    # wait that lands right in front of an LDS read is one the compiler put
+    # there because it could not tell the read's stage from a stage still
+    # being loaded; it waits for every load in flight.  (A loop over the
+    # last slices of a tile with run-time conditions got one before each
+    # fragment read.)
+    funcs = _direct_load_kernels(asm["gemm_mfma.hip"])
+    assert len(funcs) == 4, sorted(funcs)
+    mem = re.compile(r"(ds_|global_|buffer_|s_barrier|s_endpgm)")
+    for name, body in funcs.items():
+        lines = [x.split(";")[0].strip() for x in body.splitlines()]
+        lines = [x for x in lines if x and not x.endswith(":")]
+        waits = 0
+        for i, x in enumerate(lines):
+            if not (x.startswith("s_waitcnt") and "vmcnt" in x):
+                continue
+            nxt = next((y for y in lines[i + 1:] if mem.match(y)), "")
+            assert not nxt.startswith("ds_read"), f"{name}: '{x}' right before '{nxt}'"
+            waits += nxt == "s_barrier"
+        assert waits >= 8, f"{name}: {waits} explicit waits"
+
+
 def test_direct_load_loops_keep_loads_in_flight(asm):
     # The direct-load kernels (gemm_mfma_f32<T, true, true>) stage slices
     # with global_load_lds_dwordx4 and wait for them with explicit counts.

@@ -605,6 +605,56 @@ __device__ __forceinline__ void dma_order() {
     dma_schedule<0, NM, (NDR + FIRST - 1) / FIRST, (Dma<T>::NV + SECOND - 1) / SECOND>();
 }
 
+// The last R slices of a tile, s .. s + R - 1 (s a multiple of S, so slice
+// s + j is in stage j % S; S <= R <= 2 S), each iteration J a copy of its
+// own: slices s + S .. s + R - 1 are still to load (the one past K, if
+// any, with its check), and each wait is for exactly the slice that the
+// next iteration reads, so the last load has landed two iterations before
+// the end and the kernel ends with no load in flight.  A loop over these
+// iterations with run-time conditions made the compiler wait for every
+// load in flight before each fragment read (it could no longer tell the
+// stages apart): 1024^3 1.7%, 1024^2 x 1000 6% and 16384 x 64 x 2048 5%
+// slower.
+template <class T, bool TAIL, int R, int J = 0>
+__device__ __forceinline__ void dma_last(const Ctx<T> &c, const DmaLane<T> &d,
+                                         float *const *stg, int kbase, Frag<T> (&fr)[2],
+                                         f32x16 (&acc)[T::FM][T::FN], int64_t s) {
+    if constexpr (J < R) {
+        using D = Dma<T>;
+        constexpr int S = D::S;
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (J + 1 < R) dma_frags<T>(d, stg[(J + 1) % S], kbase, fr[(J + 1) & 1]);
+        mfmas<T, 0, T::HALF>(fr[J & 1], acc);
+        if constexpr (J + S < R) {
+            if constexpr (TAIL && J + S == R - 1)
+                dma_issue_tail<T>(d, stg[J % S], (s + J + S) * T::BK, c.K, c.ldb, c.t);
+            else
+                dma_issue<T>(d, stg[J % S], (s + J + S) * T::BK, c.ldb);
+            dma_order<T>();
+        }
+        if constexpr (J + 3 <= R) {
+            // slice s + J + 2 is in; the slices after it up to the last
+            // one issued may still be on their way
+            constexpr int LAST = J + S < R - 1 ? J + S : R - 1;
+            dma_sync<(LAST - J - 2) * D::NV>();
+        }
+        dma_last<T, TAIL, R, J + 1>(c, d, stg, kbase, fr, acc, s);
+    }
+}
+
+// dma_last for the run-time count r, S <= r <= 2 S (wave-uniform).
+template <class T, bool TAIL, int R>
+__device__ __forceinline__ void dma_last_r(int r, const Ctx<T> &c, const DmaLane<T> &d,
+                                           float *const *stg, int kbase, Frag<T> (&fr)[2],
+                                           f32x16 (&acc)[T::FM][T::FN], int64_t s) {
+    if constexpr (R <= 2 * Dma<T>::S) {
+        if (r == R)
+            dma_last<T, TAIL, R>(c, d, stg, kbase, fr, acc, s);
+        else
+            dma_last_r<T, TAIL, R + 1>(r, c, d, stg, kbase, fr, acc, s);
+    }
+}
+
 // The K loop over the n slices of a tile when every load is an aligned
 // float4 inside the matrices (A and B rows 16-byte aligned, the tile
 // inside) and every slice is full -- or, with TAIL, every slice but the
@@ -618,15 +668,44 @@ __device__ __forceinline__ void k_loop_dma(const Ctx<T> &c, float *const *stg, i
     constexpr int S = D::S, BK = T::BK;
     const DmaLane<T> d = dma_lane<T>(c, arow, bcol, kbase);
     Frag<T> fr[2];
-    // prologue: slices 0 .. S-1 in flight; wait for 0 and 1, read the
-    // fragments of 0, and let every wave finish that read before
-    // iteration 0 reloads stage 0
+    // prologue: slices 0 .. S-1 in flight
 #pragma unroll
     for (int j = 0; j < S; ++j) dma_issue<T>(d, stg[j], j * BK, c.ldb);
-    dma_sync<(S - 2) * D::NV>();
-    dma_frags<T>(d, stg[0], kbase, fr[0]);
-    dma_sync<(S - 2) * D::NV>();
     int64_t s = 0;
+    if constexpr (S == 4) {
+        // the MFMAs of slice 0 start once it has landed; slice 1 is waited
+        // for halfway through them, at a barrier that also ends every
+        // wave's reading of stage 0 before iteration 0 reloads it; then the
+        // rest of the first round (slices S + 1 .. 2 S - 1 are inside, as
+        // n >= 2 S + 1).  Against waiting for slices 0 and 1 first: 1024^3
+        // +0.7%, 1024^2 x 512 +1.2%, 1024^2 x 1000 +0.9%; on the 6-stage
+        // ring the same start was 0.1 to 0.9% slower, so that keeps the
+        // plain prologue
+        dma_sync<(S - 1) * D::NV>();
+        dma_frags<T>(d, stg[0], kbase, fr[0]);
+        mfmas<T, 0, T::HALF / 2>(fr[0], acc);
+        dma_sync<(S - 2) * D::NV>();
+        dma_frags<T>(d, stg[1], kbase, fr[1]);
+        mfmas<T, T::HALF / 2, T::HALF>(fr[0], acc);
+        dma_issue<T>(d, stg[0], S * BK, c.ldb);
+        dma_sync<(S - 2) * D::NV>();
+#pragma unroll
+        for (int u = 1; u < S; ++u) {
+            __builtin_amdgcn_sched_barrier(0);
+            dma_frags<T>(d, stg[(u + 1) % S], kbase, fr[(u + 1) & 1]);
+            mfmas<T, 0, T::HALF>(fr[u & 1], acc);
+            dma_issue<T>(d, stg[u], (u + S) * BK, c.ldb);
+            dma_order<T>();
+            dma_sync<(S - 2) * D::NV>();
+        }
+        s = S;
+    } else {
+        // wait for slices 0 and 1, read the fragments of 0, and let every
+        // wave finish that read before iteration 0 reloads stage 0
+        dma_sync<(S - 2) * D::NV>();
+        dma_frags<T>(d, stg[0], kbase, fr[0]);
+        dma_sync<(S - 2) * D::NV>();
+    }
     // with TAIL the last slice is left to the loop below, which checks it
     int64_t loads = n;
     if constexpr (TAIL) loads = n - 1;
@@ -641,34 +720,9 @@ __device__ __forceinline__ void k_loop_dma(const Ctx<T> &c, float *const *stg, i
             dma_sync<(S - 2) * D::NV>();
         }
     }
-    // the last iterations: a slice past the end reloads the last slice into
-    // a stage that is not read again, so that every iteration issues the
-    // same loads and waits for the same count (waiting for every load here
-    // instead exposed a load's whole latency once per tile when n is not a
-    // multiple of S: 1024^2 x 1008 and x 1040 1.7% and 3% slower); all
-    // loads have landed before the kernel ends
-    for (; s < n; s += S) {
-#pragma unroll
-        for (int u = 0; u < S; ++u) {
-            if (s + u < n) {
-                __builtin_amdgcn_sched_barrier(0);
-                if (s + u + 1 < n) dma_frags<T>(d, stg[(u + 1) % S], kbase, fr[(u + 1) & 1]);
-                __builtin_amdgcn_sched_barrier(0);
-                mfmas<T, 0, T::HALF>(fr[u & 1], acc);
-                const int64_t next = s + u + S < n ? s + u + S : n - 1;
-                if constexpr (TAIL) {
-                    if (next == n - 1)
-                        dma_issue_tail<T>(d, stg[u], next * BK, c.K, c.ldb, c.t);
-                    else
-                        dma_issue<T>(d, stg[u], next * BK, c.ldb);
-                } else {
-                    dma_issue<T>(d, stg[u], next * BK, c.ldb);
-                }
-                dma_sync<(S - 2) * D::NV>();
-            }
-        }
-    }
-    wait_vm_lgkm0<0>();
+    // the last R = n - s slices, S <= R <= 2 S (n >= 2 S + 1; with TAIL
+    // R >= S + 1, so the slice past K is loaded there)
+    dma_last_r<T, TAIL, S>(static_cast<int>(n - s), c, d, stg, kbase, fr, acc, s);
 }
 
 // How the work of one launch is cut up.  Logical tiles [0, sk_tiles) --
