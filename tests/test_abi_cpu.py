@@ -68,10 +68,10 @@ def test_describe_plans():
     d = tra.tra_gemm_describe(tra.MFMA, 2048, 2048, 2048)
     assert "tile=128x128x16" in d and "8 waves" in d and "grid=256" in d and "block=512" in d
     # the 64 x 64 tiles with K a multiple of 16 and aligned rows: direct
-    # loads into 4 (6 for the deep tile) LDS stages of 8448 bytes
+    # loads into 6 LDS stages of 8448 bytes
     d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 1024)
-    assert "tile=64x64x16" in d and "4 LDS stages" in d and "grid=256" in d and "block=256" in d
-    assert "lds_bytes=33792" in d
+    assert "tile=64x64x16" in d and "6 LDS stages" in d and "grid=256" in d and "block=256" in d
+    assert "lds_bytes=50688" in d
     d = tra.tra_gemm_describe(tra.MFMA, 16384, 64, 16384)
     assert "tile=64x64x16" in d and "6 LDS stages" in d and "grid=256" in d
     assert "lds_bytes=50688" in d
@@ -83,12 +83,15 @@ def test_describe_plans():
     assert "<64x64x16, 4 waves>" in d and "lds_bytes=18944" in d
     # K a multiple of 4 but not of 16: direct loads, the last slice checked
     d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 1000)
-    assert "4 LDS stages" in d and "lds_bytes=33792" in d
-    # fewer than 32 slices: register-staged
-    d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 496)
-    assert "<64x64x16, 4 waves>" in d
-    d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 512)
-    assert "4 LDS stages" in d
+    assert "6 LDS stages" in d and "lds_bytes=50688" in d
+    # fewer than the 13 slices (2 x 6 + 1) the direct-load loop needs:
+    # register-staged
+    d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 192)
+    assert "<64x64x16, 4 waves>" in d and "lds_bytes=18944" in d
+    d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 208)
+    assert "6 LDS stages" in d
+    d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 196)    # 13 slices, the last past K
+    assert "6 LDS stages" in d
     d = tra.tra_gemm_describe(tra.NAIVE, 1024, 1024, 1024)
     assert "gemm_naive_f32" in d and "grid=4096" in d and "block=256" in d
     d = tra.tra_gemm_describe(tra.LDS_TILED, 1024, 1024, 1024)
@@ -339,7 +342,7 @@ def test_auto_choice(shape, rung):
 
 
 @pytest.mark.parametrize("shape,tile", [
-    ((1024, 1024, 1024), "<64x64x16, 4 waves, 4 LDS stages>"),     # K <= 1024
+    ((1024, 1024, 1024), "<64x64x16, 4 waves, 6 LDS stages>"),     # K <= 1024
     ((3000, 2049, 1531), "<64x64x16, 4 waves, 4 sets>"),    # 128x128 would waste the edge
     ((4096, 4096, 4096), "<256x128x16, 8 waves, 4 sets>"),  # 4 tiles of 128x128 a CU
     ((4096, 2048, 1024), "<256x128x16, 8 waves, 4 sets>"),  # exactly 256 tiles of 256x128
@@ -347,7 +350,7 @@ def test_auto_choice(shape, rung):
     ((2048, 2048, 2048), "<128x128x16, 8 waves>"),          # one 128x128 tile a CU
     ((2304, 2304, 2304), "<128x128x16, 8 waves>"),          # 324 tiles, long K: parts
     ((2000, 2600, 3000), "<128x128x16, 8 waves>"),          # 336 tiles, edges wasted no worse
-    ((3000, 3000, 1000), "<64x64x16, 4 waves, 4 LDS stages>"),     # short K stays on 64x64
+    ((3000, 3000, 1000), "<64x64x16, 4 waves, 6 LDS stages>"),     # short K stays on 64x64
     ((3072, 3072, 3072), "<64x64x16, 4 waves, 6 LDS stages>"),     # 576 tiles: 2.25 a CU
 ])
 def test_auto_tile_class(shape, tile):
@@ -383,10 +386,9 @@ def test_split_plans_hold_their_invariants():
         elif form == "parts":
             parts = wgs // sk
             assert wgs == sk * parts and 2 <= parts <= 8 and 2 * parts <= ipt
-            # the deep 64 x 64 tile (4 register sets, or 6 LDS stages when it
-            # loads directly) is planned at three workgroups a CU
-            plain = tra.tra_gemm_describe(tra.MFMA, M, N, K)
-            deep = "4 sets" in plain or "6 LDS stages" in plain
+            # the deep 64 x 64 tile (4 register sets; a split launch stages
+            # through registers) is planned at three workgroups a CU
+            deep = "4 sets" in tra.tra_gemm_describe(tra.MFMA_STREAMK, M, N, K)
             wave = 256 * (1 if block == 512 else (3 if deep else 4))
             assert sk == tiles % wave and wgs <= wave
             assert grid == tiles + sk * (parts - 1) and ws == wgs * bm * bn * 4

@@ -41,12 +41,14 @@ SHAPES = [
     (1000, 1000, 1007),   # register-blocked rung: K split over 3 lane groups, K tail
     (300, 700, 255),      # register-blocked rung: K split over 4 lane groups
     (100, 200, 127),      # register-blocked rung: K split over 2 lane groups
-    (1000, 1000, 528),    # direct loads into LDS, 64 x 64, 4 stages
-    (700, 900, 1536),     # direct loads, 64 x 64, 6 stages
+    (1000, 1000, 528),    # direct loads into LDS, 64 x 64, K <= 1024
+    (700, 900, 1536),     # direct loads, K > 1024
     (64, 64, 1040),       # direct loads, one tile
     (200, 300, 4112),     # direct loads, few tiles, long K
+    (1000, 1000, 208),    # direct loads, the fewest slices (13)
     (1000, 1000, 1000),   # direct loads, the last slice past K
-    (700, 900, 1548),     # direct loads, 6 stages, the last slice past K
+    (700, 900, 1548),     # direct loads, the last slice past K
+    (300, 500, 260),      # direct loads, the last slice past K, 17 slices
 ]
 
 

@@ -294,20 +294,27 @@ def test_tile_shapes_with_tails(variant, shape):
 # (edge tiles moved inside), at the fewest slices that take it and one more,
 # and one tile alone: (M, N, K, kernel the MFMA rung plans).  The
 # stream-K form of the same shapes runs register-staged.
+# R below: the slices left for the unrolled last iterations (6 to 12)
+_DMA = "<64x64x16, 4 waves, 6 LDS stages>"
 DMA_SHAPES = [
-    (1000, 1000, 1024, "<64x64x16, 4 waves, 4 LDS stages>"),
-    (1000, 1000, 512, "<64x64x16, 4 waves, 4 LDS stages>"),    # 32 slices: the fewest
-    (1000, 1000, 528, "<64x64x16, 4 waves, 4 LDS stages>"),    # 33: a tail of 5
-    (64, 64, 560, "<64x64x16, 4 waves, 4 LDS stages>"),        # one tile, a tail of 7
-    (700, 900, 1536, "<64x64x16, 4 waves, 6 LDS stages>"),
-    (64, 64, 1040, "<64x64x16, 4 waves, 6 LDS stages>"),       # 65 slices, one tile
-    (3000, 2052, 1536, "<64x64x16, 4 waves, 6 LDS stages>"),   # 1551 tiles
-    (200, 300, 4112, "<64x64x16, 4 waves, 6 LDS stages>"),     # 20 tiles, long K
+    (1000, 1000, 1024, _DMA),     # R = 10
+    (1000, 1000, 208, _DMA),      # 13 slices, the fewest; R = 7
+    (1000, 1000, 224, _DMA),      # R = 8
+    (1000, 1000, 528, _DMA),      # R = 9
+    (64, 64, 560, _DMA),          # one tile, R = 11
+    (700, 900, 1536, _DMA),       # R = 6
+    (64, 64, 1040, _DMA),         # 65 slices, one tile
+    (3000, 2052, 1536, _DMA),     # 1551 tiles
+    (200, 300, 4112, _DMA),       # 20 tiles, long K
     # K a multiple of 4 but not of 16: the last slice runs past K
-    (1000, 1000, 1000, "<64x64x16, 4 waves, 4 LDS stages>"),   # 8 of its 16 k inside
-    (1000, 1000, 516, "<64x64x16, 4 waves, 4 LDS stages>"),    # 4 inside, 33 slices
-    (700, 900, 1548, "<64x64x16, 4 waves, 6 LDS stages>"),     # 12 inside
-    (64, 64, 1044, "<64x64x16, 4 waves, 6 LDS stages>"),       # one tile, 4 inside
+    (1000, 1000, 1000, _DMA),     # 8 of its 16 k inside, R = 9
+    (1000, 1000, 516, _DMA),      # 4 inside
+    (700, 900, 1548, _DMA),       # 12 inside, R = 7
+    (64, 64, 1044, _DMA),         # one tile, R = 12
+    (1000, 1000, 196, _DMA),      # 13 slices, R = 7
+    (1000, 1000, 212, _DMA),      # R = 8
+    (300, 500, 244, _DMA),        # R = 10
+    (300, 500, 260, _DMA),        # R = 11
 ]
 
 
@@ -587,16 +594,16 @@ def test_random_shapes_small_ints_exact(variant):
 
 def _random_direct_load_shapes(seed, n):
     # shapes whose MFMA launch stages with direct loads: M, N >= 64, N a
-    # multiple of 4, K with at least 32 slices (4 stages, K <= 1024) or more
-    # than 64 (6 stages), a multiple of 16 or only of 4 (the last slice
-    # running past K); leading dimensions padded by
-    # whole quads, so rows stay 16-byte aligned
+    # multiple of 4, K with at least 13 slices (K <= 1024, or more than 64
+    # slices), a multiple of 16 or only of 4 (the last slice running past
+    # K); leading dimensions padded by whole quads, so rows stay 16-byte
+    # aligned
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
         M = int(rng.integers(64, 700))
         N = 4 * int(rng.integers(16, 175))
-        K = 16 * int(rng.integers(32, 65) if i % 2 == 0 else rng.integers(65, 100))
+        K = 16 * int(rng.integers(13, 65) if i % 2 == 0 else rng.integers(65, 100))
         if i % 4 >= 2:
             K -= 4 * int(rng.integers(1, 4))   # the last slice runs past K
         pads = tuple(4 * int(x) for x in rng.integers(0, 3, size=3))
@@ -606,9 +613,9 @@ def _random_direct_load_shapes(seed, n):
 
 @pytest.mark.parametrize("variant", [tra.AUTO, tra.MFMA], ids=["auto", "mfma"])
 def test_random_direct_load_shapes_exact(variant):
-    """Seeded random shapes through the direct-load K loop (both stage
-    counts, edge tiles moved inside, padded rows): exact on small integers,
-    and C untouched past column N."""
+    """Seeded random shapes through the direct-load K loop (both 64 x 64
+    classes, edge tiles moved inside, padded rows): exact on small
+    integers, and C untouched past column N."""
     for M, N, K, (pa, pb, pc) in _random_direct_load_shapes(77, 16):
         assert "LDS stages" in tra.tra_gemm_describe(tra.MFMA, M, N, K), (M, N, K)
         log(f"[case] direct loads {tra.tra_gemm_variant_name(variant)} {M}x{N}x{K} "

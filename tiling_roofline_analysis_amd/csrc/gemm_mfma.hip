@@ -423,14 +423,18 @@ __device__ __forceinline__ void k_loop(const Ctx<T> &c, float *lds, int arow, in
 // were read in iteration s-1, before the barrier that ended it).  It ends
 // by waiting for this wave's loads of slice s+2 and a workgroup barrier,
 // after which every wave's share of slice s+2 is in LDS and every wave has
-// read the fragments of slice s+1.  S-2 slices stay in flight across a
-// barrier: 2 for the Many tile, 4 for the Deep tile, whose shapes stream A
-// from HBM (16384 x 64 x 16384 lost 23% against the register path with 4
-// stages; 6 stages also keep three workgroups a CU, as the register-staged
-// Deep kernel has, where 8 would allow two).  The Many tile lost 2% with 6.
-// Timed against the register path (medians of interleaved rounds, two
-// boxes): 1024^3 +1.2 to +2.3%, 1024^2 x 512 +1.6%, 3072^2 x 2048 +2.7%,
-// 1536 x 2048 x 2048 +1.8%, 16384 x 64 x 16384 +0.3%.  The 8-wave tiles
+// read the fragments of slice s+1.  S = 6, so 4 slices stay in flight
+// across a barrier (with 4 stages 16384 x 64 x 16384, which streams A from
+// HBM, lost 23% against the register path, and 1024^3, 2048 x 1024 x 512
+// and 3000^2 x 1000 ran 0.8 to 1.4% slower than with 6; 8 stages gained
+// 1.4% on 16384 x 64 x 16384 and lost up to 0.5% elsewhere).  Six stages of
+// 8448 bytes let three workgroups share a CU.  With no register sets the
+// kernel is the same for the Many and Deep tiles, so both launch one
+// instantiation (DmaTile).  Timed against the register path (medians of
+// 7 interleaved rounds, one box): 1024^3 +4.5%, 1024^2 x 512 +4.4%,
+// 2048 x 1024 x 512 +4.9%, 3000^2 x 1000 +3.9%, 3072^2 x 2048 +2.2%,
+// 16384 x 64 x 2048 +1.5%; 16384 x 64 x 16384, which HBM and power hold,
+// within 0.4%.  The 8-wave tiles
 // keep the register path: their loop already runs at 98% of the MFMA rate
 // at 4096^3 (direct loads: within 0.2%), and the 128 x 128 tile's ring
 // would let two workgroups share a CU where its registers allow one
@@ -438,7 +442,7 @@ __device__ __forceinline__ void k_loop(const Ctx<T> &c, float *lds, int arow, in
 template <class T>
 struct Dma {
     static constexpr bool USED = T::BM == 64;               // the 64 x 64 tiles only
-    static constexpr int S = T::NR == 4 ? 6 : 4;            // stages
+    static constexpr int S = 6;                             // stages
     static constexpr int RPB = 256 / T::BN;                 // B rows per block
     static constexpr int PADB = 32 * RPB / T::HALF;         // words between B blocks
     static constexpr int A_WORDS = T::BM * T::BK;
@@ -457,6 +461,11 @@ struct Dma {
     static_assert((S - 2) * NV < 64 && S >= 4 && S <= 8 && S % 2 == 0,
                   "vmcnt range, stage arrays, fragment buffers alternate");
 };
+
+// The tile a direct-load launch of tile T runs: T with two register sets,
+// which direct staging does not use.
+template <class T>
+using DmaTile = MfmaTile<T::BM, T::BN, T::BK, T::WM, T::WN, 2>;
 
 // s_waitcnt vmcnt(VM) lgkmcnt(0), expcnt not waited for (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
@@ -671,42 +680,13 @@ __device__ __forceinline__ void k_loop_dma(const Ctx<T> &c, float *const *stg, i
     // prologue: slices 0 .. S-1 in flight
 #pragma unroll
     for (int j = 0; j < S; ++j) dma_issue<T>(d, stg[j], j * BK, c.ldb);
+    // wait for slices 0 and 1, read the fragments of 0, and let every wave
+    // finish that read before iteration 0 reloads stage 0
+    dma_sync<(S - 2) * D::NV>();
+    dma_frags<T>(d, stg[0], kbase, fr[0]);
+    dma_sync<(S - 2) * D::NV>();
     int64_t s = 0;
-    if constexpr (S == 4) {
-        // the MFMAs of slice 0 start once it has landed; slice 1 is waited
-        // for halfway through them, at a barrier that also ends every
-        // wave's reading of stage 0 before iteration 0 reloads it; then the
-        // rest of the first round (slices S + 1 .. 2 S - 1 are inside, as
-        // n >= 2 S + 1).  Against waiting for slices 0 and 1 first: 1024^3
-        // +0.7%, 1024^2 x 512 +1.2%, 1024^2 x 1000 +0.9%; on the 6-stage
-        // ring the same start was 0.1 to 0.9% slower, so that keeps the
-        // plain prologue
-        dma_sync<(S - 1) * D::NV>();
-        dma_frags<T>(d, stg[0], kbase, fr[0]);
-        mfmas<T, 0, T::HALF / 2>(fr[0], acc);
-        dma_sync<(S - 2) * D::NV>();
-        dma_frags<T>(d, stg[1], kbase, fr[1]);
-        mfmas<T, T::HALF / 2, T::HALF>(fr[0], acc);
-        dma_issue<T>(d, stg[0], S * BK, c.ldb);
-        dma_sync<(S - 2) * D::NV>();
-#pragma unroll
-        for (int u = 1; u < S; ++u) {
-            __builtin_amdgcn_sched_barrier(0);
-            dma_frags<T>(d, stg[(u + 1) % S], kbase, fr[(u + 1) & 1]);
-            mfmas<T, 0, T::HALF>(fr[u & 1], acc);
-            dma_issue<T>(d, stg[u], (u + S) * BK, c.ldb);
-            dma_order<T>();
-            dma_sync<(S - 2) * D::NV>();
-        }
-        s = S;
-    } else {
-        // wait for slices 0 and 1, read the fragments of 0, and let every
-        // wave finish that read before iteration 0 reloads stage 0
-        dma_sync<(S - 2) * D::NV>();
-        dma_frags<T>(d, stg[0], kbase, fr[0]);
-        dma_sync<(S - 2) * D::NV>();
-    }
-    // with TAIL the last slice is left to the loop below, which checks it
+    // with TAIL the slice past K is left to dma_last, which checks it
     int64_t loads = n;
     if constexpr (TAIL) loads = n - 1;
     for (; s + S - 1 + S < loads; s += S) {
@@ -1320,18 +1300,14 @@ int64_t main_grid(const Split &r) {
 
 // How the main launch stages its slices: 0 through registers; with direct
 // loads when every tile lies inside the matrices with float4 rows
-// (aligned_launch) and there are at least 32 slices -- 1 when every slice
-// is full, 2 when the last one runs past K and K is a multiple of 4 (so a
-// quad of A along k is wholly inside or outside the matrix).  (Shorter K
-// lost to the register path, most where a CU runs many short tiles:
-// 5265 x 2016 x 240, 15 slices, 7%; 4849 x 1608 x 496, 31 slices, 1%;
-// 1024^2 x 128 1%.  From 32 slices on it gained: 1024^2 x 512 +0.8 to
-// 1.6%, 5308 x 1328 x 528 +0.5%, 2403 x 4156 x 880 +0.5%.)  The K loop
-// itself needs 2 S + 1 slices.
-constexpr int64_t kDmaMinSlices = 32;
+// (aligned_launch) and there are the 2 S + 1 slices the direct-load K loop
+// needs -- 1 when every slice is full, 2 when the last one runs past K and
+// K is a multiple of 4 (so a quad of A along k is wholly inside or outside
+// the matrix).  Short K gains most: 1024^2 x 208 (13 slices) +8%,
+// 5264 x 2016 x 240 +5%, 4848 x 1608 x 496 +5%, 2048 x 1024 x 256 +4.5%.
 inline int dma_mode(bool aligned, int64_t K, int64_t bk, int64_t stages) {
     const int64_t n = ceil_div(K, bk);
-    if (!aligned || n < kDmaMinSlices || n < 2 * stages + 1) return 0;
+    if (!aligned || n < 2 * stages + 1) return 0;
     if (K % bk == 0) return 1;
     return K % 4 == 0 ? 2 : 0;
 }
@@ -1406,19 +1382,19 @@ hipError_t launch_tile(const GemmArgs &a, bool stream_k, void *ws, size_t ws_byt
     // register-staged kernel, and a stage ring that changes how many
     // workgroups a CU holds breaks them (2560^3, 128 x 128 tiles with
     // stream-K runs, went from 256 to 402 us when direct loads let two
-    // workgroups share a CU; the 64 x 64 rings now hold as many as the
-    // register-staged kernels, four and three)
+    // workgroups share a CU; the 64 x 64 ring holds three a CU, where the
+    // register-staged kernels hold four and three)
     const bool aligned = aligned_launch<T>(a, vec_a, vec_b);
     if constexpr (Dma<T>::USED) {
         const int mode = p.sk_tiles == 0 ? dma_mode(aligned, a.K, T::BK, Dma<T>::S) : 0;
         if (mode == 1)
-            hipLaunchKernelGGL((gemm_mfma_f32<T, true, 1>), grid, dim3(T::THREADS), 0, a.stream,
-                               a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, p, vec_a,
-                               vec_b, vec_c);
+            hipLaunchKernelGGL((gemm_mfma_f32<DmaTile<T>, true, 1>), grid, dim3(T::THREADS), 0,
+                               a.stream, a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, p,
+                               vec_a, vec_b, vec_c);
         else if (mode == 2)
-            hipLaunchKernelGGL((gemm_mfma_f32<T, true, 2>), grid, dim3(T::THREADS), 0, a.stream,
-                               a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, p, vec_a,
-                               vec_b, vec_c);
+            hipLaunchKernelGGL((gemm_mfma_f32<DmaTile<T>, true, 2>), grid, dim3(T::THREADS), 0,
+                               a.stream, a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, p,
+                               vec_a, vec_b, vec_c);
         if (mode != 0) return hipGetLastError();
     }
     if (aligned)
@@ -1442,7 +1418,7 @@ LaunchPlan plan_mfma(int64_t M, int64_t N, int64_t K, bool stream_k) {
                                      nullptr);
         case Shape::kMany:
             return plan_for<TileMany>(M, N, K, stream_k, "gemm_mfma_f32<64x64x16, 4 waves>",
-                                      "gemm_mfma_f32<64x64x16, 4 waves, 4 LDS stages>");
+                                      "gemm_mfma_f32<64x64x16, 4 waves, 6 LDS stages>");
         default:
             return plan_for<TileDeep>(M, N, K, stream_k,
                                       "gemm_mfma_f32<64x64x16, 4 waves, 4 sets>",
