@@ -95,8 +95,9 @@ typedef enum tra_status {
  *                (v_mfma_f32_32x32x2_f32), tile shape chosen from the
  *                problem shape, one tile per workgroup; slices staged
  *                through registers into two LDS buffers, or, on the 64x64
- *                tiles when rows are 16-byte aligned and K is a multiple of
- *                4, loaded straight into a ring of LDS stages.
+ *                tiles when rows are 16-byte aligned, K is a multiple of 4
+ *                and there are at least 13 slices of 16, loaded straight
+ *                into a ring of six LDS stages.
  *   MFMA_STREAMK the MFMA kernel with the tile count decoupled from the
  *                workgroup count.  When the tiles do not fill whole waves
  *                of resident workgroups (the tile-size versus occupancy
