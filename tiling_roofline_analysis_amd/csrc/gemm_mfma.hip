@@ -427,18 +427,18 @@ __device__ __forceinline__ void k_loop(const Ctx<T> &c, float *lds, int arow, in
 // across a barrier (with 4 stages 16384 x 64 x 16384, which streams A from
 // HBM, lost 23% against the register path, and 1024^3, 2048 x 1024 x 512
 // and 3000^2 x 1000 ran 0.8 to 1.4% slower than with 6; 8 stages gained
-// 1.4% on 16384 x 64 x 16384 and lost up to 0.5% elsewhere).  Six stages of
-// 8448 bytes let three workgroups share a CU.  With no register sets the
-// kernel is the same for the Many and Deep tiles, so both launch one
+// 1.5% on 16384 x 64 x 16384 but lost 1% at 1024^3, 1.8% at
+// 2048 x 1024 x 512 and 4.4% at 5264 x 2016 x 240).  Six stages of 8448
+// bytes let three workgroups share a CU.  With no register sets the kernel
+// is the same for the Many and Deep tiles, so both launch one
 // instantiation (DmaTile).  Timed against the register path (medians of
 // 7 interleaved rounds, one box): 1024^3 +4.5%, 1024^2 x 512 +4.4%,
 // 2048 x 1024 x 512 +4.9%, 3000^2 x 1000 +3.9%, 3072^2 x 2048 +2.2%,
 // 16384 x 64 x 2048 +1.5%; 16384 x 64 x 16384, which HBM and power hold,
-// within 0.4%.  The 8-wave tiles
-// keep the register path: their loop already runs at 98% of the MFMA rate
-// at 4096^3 (direct loads: within 0.2%), and the 128 x 128 tile's ring
-// would let two workgroups share a CU where its registers allow one
-// (2048^3 and 2560^3 1% slower).
+// within 0.4%.  The 8-wave tiles keep the register path: their loop
+// already runs at 98% of the MFMA rate at 4096^3 (direct loads: within
+// 0.2%), and the 128 x 128 tile's ring would let two workgroups share a CU
+// where its registers allow one (2048^3 and 2560^3 1% slower).
 template <class T>
 struct Dma {
     static constexpr bool USED = T::BM == 64;               // the 64 x 64 tiles only
