@@ -92,6 +92,12 @@ def test_describe_plans():
     assert "6 LDS stages" in d
     d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 196)    # 13 slices, the last past K
     assert "6 LDS stages" in d
+    # direct loads address a lane's quad by a byte offset from the tile's
+    # corner below 2^31: 64 rows of A 2^23 floats apart (lda = K) are too far
+    d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, 1 << 23)
+    assert "<64x64x16, 4 waves, 4 sets>" in d
+    d = tra.tra_gemm_describe(tra.MFMA, 1024, 1024, (1 << 23) - 4)
+    assert "6 LDS stages" in d
     d = tra.tra_gemm_describe(tra.NAIVE, 1024, 1024, 1024)
     assert "gemm_naive_f32" in d and "grid=4096" in d and "block=256" in d
     d = tra.tra_gemm_describe(tra.LDS_TILED, 1024, 1024, 1024)

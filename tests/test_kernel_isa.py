@@ -146,27 +146,35 @@ def test_direct_load_fragment_reads_wait_only_at_barriers(asm):
 
 
 def test_direct_load_loops_keep_loads_in_flight(asm):
-    # The direct-load kernels (gemm_mfma_f32<T, true, true>) stage slices
-    # with global_load_lds_dwordx4 and wait for them with explicit counts.
-    # Their main loop must not wait for every load in flight (vmcnt(0)):
-    # that is what the compiler inserts before an LDS read that may alias
-    # an earlier direct load, and it would serialise the pipeline.
+    # The direct-load kernels (gemm_mfma_f32<T, true, 1 or 2>) stage slices
+    # with buffer_load_dwordx4 ... lds and wait for them with explicit
+    # counts.  Their main loop must not wait for every load in flight
+    # (vmcnt(0)): that is what the compiler inserts before an LDS read that
+    # may alias an earlier direct load, and it would serialise the pipeline.
+    # It must not compute vector addresses either: each slice moves only the
+    # buffer's uniform base (scalar adds), since 64-bit vector adds beside
+    # the MFMAs cost 6% at 1024^3.
     funcs = {n: b for n, b in _functions(asm["gemm_mfma.hip"]).items()
              if n.startswith("_ZN3tra12_GLOBAL__N_113gemm_mfma_f32INS0_8MfmaTile")
              and re.search(r"Lb1ELi[12]EEEvlllPKflS5_lPflNS0_6SkPlanEiii$", n)}
     # the 64 x 64 tile (both 64 x 64 classes launch it), with full slices
     # and with a slice past K
     assert len(funcs) == 2, sorted(funcs)
+    dma = re.compile(r"^\s+buffer_load_dwordx4 .* lds\s*$", re.M)
     for name, body in funcs.items():
         code = "\n".join(line.split(";")[0] for line in body.splitlines())
-        assert "global_load_lds_dwordx4" in code, name
+        assert dma.search(code), name
         # every direct load writes LDS at the address in M0, so the kernel
         # sets M0 (a compiler of this family has been seen to drop that for
         # a direct load into an LDS array at a constant address)
         assert re.search(r"^\s+s_\w+\s+m0,", code, re.M), f"{name}: M0 never set"
-        main = [lp for lp in _loops(body) if "global_load_lds_dwordx4" in lp
+        main = [lp for lp in _loops(body)
+                if dma.search("\n".join(x.split(";")[0] for x in lp.splitlines()))
                 and "v_mfma_f32_32x32x2_f32" in lp]
         assert main, f"{name}: no loop with direct loads and MFMAs"
         lp = "\n".join(line.split(";")[0] for line in main[0].splitlines())
         assert "vmcnt(0)" not in lp, f"{name}: main loop waits for every load in flight"
         assert re.search(r"s_waitcnt vmcnt\([1-9]\d*\) lgkmcnt\(0\)", lp), name
+        valu = [x.strip() for x in lp.splitlines()
+                if re.match(r"\s+v_", x) and not re.match(r"\s+v_mfma", x)]
+        assert len(valu) <= 2, f"{name}: vector work in the main loop: {valu}"

@@ -494,10 +494,27 @@ __device__ __forceinline__ void dma16(const float *src, float *dst) {
     __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
 
+// The same through a buffer resource: 16 bytes per lane from base + voff
+// bytes (base wave-uniform, voff < 2^31 per lane; word 3 of the resource,
+// 0x00020000, is the 32-bit data format that gfx9 raw buffer loads take).
+// The per-lane part of the address then stays one 32-bit register for the
+// whole K loop and each slice moves only the uniform base, in scalar
+// registers: the 64-bit vector adds that global loads need per slice
+// competed with the MFMAs (1024^3 6.1%, 512 x 4096 x 4096 6.1% and
+// 1024^2 x 2048 6.7% slower with them).
+__device__ __forceinline__ void dma16b(const float *base, uint32_t voff, float *dst) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, 0x7fffffff, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+}
+
 template <class T>
 struct DmaLane {
     const float *pa[Dma<T>::A_INS];   // this lane's A quad of slice 0, per instruction
     const float *pb[Dma<T>::B_INS];   // this lane's B quad of slice 0
+    uint32_t oa[Dma<T>::A_INS];       // the same as byte offsets from the tile's corner
+    uint32_t ob[Dma<T>::B_INS];
+    const float *abase, *bbase;       // the tile's corner: A at row m0, B at column n0
     int wa, wb;                       // the wave's first A and B block in a stage (words)
     int ra, rb;                       // this lane's fragment offsets in a stage (words)
 };
@@ -513,13 +530,17 @@ __device__ __forceinline__ DmaLane<T> dma_lane(const Ctx<T> &c, int arow, int bc
         const int g = (i * T::WAVES + wave) * 64 + lane;   // float4 of the slice's A
         const int m = g >> 2, q = (g & 3) ^ ((m >> 2) & 3);
         d.pa[i] = c.A + (c.m0 + m) * c.lda + 4 * q;
+        d.oa[i] = static_cast<uint32_t>((m * c.lda + 4 * q) * 4);
     }
 #pragma unroll
     for (int i = 0; i < D::B_INS; ++i) {
         const int g = (i * T::WAVES + wave) * 64 + lane;   // float4 of the slice's B
         const int k = g / (T::BN / 4), nq = g % (T::BN / 4);
         d.pb[i] = c.B + k * c.ldb + c.n0 + 4 * nq;
+        d.ob[i] = static_cast<uint32_t>((k * c.ldb + 4 * nq) * 4);
     }
+    d.abase = c.A + c.m0 * c.lda;
+    d.bbase = c.B + c.n0;
     d.wa = wave * 256;
     d.wb = D::A_WORDS + wave * D::B_BLOCK;
     d.ra = arow * 16;
@@ -534,10 +555,10 @@ __device__ __forceinline__ void dma_issue(const DmaLane<T> &d, float *stage, int
     using D = Dma<T>;
 #pragma unroll
     for (int i = 0; i < D::A_INS; ++i)
-        dma16(d.pa[i] + k0, stage + d.wa + i * T::WAVES * 256);
+        dma16b(d.abase + k0, d.oa[i], stage + d.wa + i * T::WAVES * 256);
 #pragma unroll
     for (int i = 0; i < D::B_INS; ++i)
-        dma16(d.pb[i] + k0 * ldb, stage + d.wb + i * T::WAVES * D::B_BLOCK);
+        dma16b(d.bbase + k0 * ldb, d.ob[i], stage + d.wb + i * T::WAVES * D::B_BLOCK);
 }
 
 // The same loads for the slice that runs past K (K a multiple of 4, so a
@@ -1305,9 +1326,13 @@ int64_t main_grid(const Split &r) {
 // K is a multiple of 4 (so a quad of A along k is wholly inside or outside
 // the matrix).  Short K gains most: 1024^2 x 208 (13 slices) +8%,
 // 5264 x 2016 x 240 +5%, 4848 x 1608 x 496 +5%, 2048 x 1024 x 256 +4.5%.
-inline int dma_mode(bool aligned, int64_t K, int64_t bk, int64_t stages) {
+inline int dma_mode(bool aligned, int64_t K, int64_t bk, int64_t stages, int64_t bm,
+                    int64_t lda, int64_t ldb) {
     const int64_t n = ceil_div(K, bk);
     if (!aligned || n < 2 * stages + 1) return 0;
+    // a lane's byte offset from the tile's corner fits the buffer loads'
+    // 31 bits (rows of A up to 8 M floats apart, of B up to 32 M)
+    if (bm * lda * 4 > INT32_MAX || bk * ldb * 4 > INT32_MAX) return 0;
     if (K % bk == 0) return 1;
     return K % 4 == 0 ? 2 : 0;
 }
@@ -1320,7 +1345,8 @@ LaunchPlan plan_for(int64_t M, int64_t N, int64_t K, bool stream_k, const char *
                     const char *dma_name) {
     const Split r = plan_split<T>(M, N, K, stream_k);
     const bool aligned = (K & 3) == 0 && M >= T::BM && N >= T::BN && (N & 3) == 0;
-    const bool dma = Dma<T>::USED && r.sk.sk_tiles == 0 && dma_mode(aligned, K, T::BK, Dma<T>::S);
+    const bool dma = Dma<T>::USED && r.sk.sk_tiles == 0 &&
+                     dma_mode(aligned, K, T::BK, Dma<T>::S, T::BM, K, N);
     LaunchPlan p{};
     p.kernel = dma ? dma_name : name;
     p.bm = T::BM;
@@ -1386,7 +1412,8 @@ hipError_t launch_tile(const GemmArgs &a, bool stream_k, void *ws, size_t ws_byt
     // register-staged kernels hold four and three)
     const bool aligned = aligned_launch<T>(a, vec_a, vec_b);
     if constexpr (Dma<T>::USED) {
-        const int mode = p.sk_tiles == 0 ? dma_mode(aligned, a.K, T::BK, Dma<T>::S) : 0;
+        const int mode =
+            p.sk_tiles == 0 ? dma_mode(aligned, a.K, T::BK, Dma<T>::S, T::BM, a.lda, a.ldb) : 0;
         if (mode == 1)
             hipLaunchKernelGGL((gemm_mfma_f32<DmaTile<T>, true, 1>), grid, dim3(T::THREADS), 0,
                                a.stream, a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, p,
