@@ -145,7 +145,29 @@ __device__ __forceinline__ void a_quad_of(int f, int &m, int &kq) {
     kq = f & 3;
 }
 
-// Loads slice k0 .. k0+BK of the A and B tiles into registers.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// A raw buffer resource over the bytes from base on (word 3, 0x00020000, is
+// the 32-bit data format that gfx9 raw buffer loads take).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const float *base) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, 0x7fffffff, 0x00020000);
+}
+
+// The float4 at base + voff bytes (voff < 2^31), through a buffer resource:
+// base is wave-uniform, so a slice's loads differ only in the scalar base
+// and each lane's 32-bit offset stays fixed over the K loop, where a
+// global load needs a 64-bit vector add per slice beside the MFMAs (4096^3
+// 1.9%, 2048^3 2.2%, 2560^3 2.5% slower).  Element loads keep the global
+// form: four 4-byte buffer loads per quad ran a third slower.
+__device__ __forceinline__ float4 bload4(const float *base, uint32_t voff) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(base), voff, 0, 0);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                       __uint_as_float(v.w));
+}
+
+// Loads slice k0 .. k0+BK of the A and B tiles into registers.  The float4
+// modes take byte offsets from the tile's corner below 2^31 (vec_a and vec_b
+// are set only then, see launch_tile).
 template <class T, int MODE>
 __device__ __forceinline__ void fetch(const Ctx<T> &c, int64_t k0, float4 (&ra)[T::A_F4],
                                       float4 (&rb)[T::B_F4]) {
@@ -156,7 +178,9 @@ __device__ __forceinline__ void fetch(const Ctx<T> &c, int64_t k0, float4 (&ra)[
         int m, kq;
         a_quad_of<T>(f, m, kq);
         const float *p = c.A + (c.m0 + m) * c.lda + k0 + 4 * kq;
-        if (MODE == kVec || MODE == kVecA) ra[r] = *reinterpret_cast<const float4 *>(p);
+        if (MODE == kVec || MODE == kVecA)
+            ra[r] = bload4(c.A + c.m0 * c.lda + k0,
+                           static_cast<uint32_t>((m * c.lda + 4 * kq) * 4));
         else if (MODE == kScalar) ra[r] = load4_scalar(p);
         else if (MODE == kEdge)
             ra[r] = load4_quad(c.A, c.lda, c.m0 + m, k0 + 4 * kq, c.m0 + m < c.M);
@@ -170,7 +194,9 @@ __device__ __forceinline__ void fetch(const Ctx<T> &c, int64_t k0, float4 (&ra)[
         if (T::B_VEC % T::THREADS != 0 && f >= T::B_VEC) break;
         const int k = f / (T::BN / 4), nq = f % (T::BN / 4);
         const float *p = c.B + (k0 + k) * c.ldb + c.n0 + 4 * nq;
-        if (MODE == kVec) rb[r] = *reinterpret_cast<const float4 *>(p);
+        if (MODE == kVec)
+            rb[r] = bload4(c.B + k0 * c.ldb + c.n0,
+                           static_cast<uint32_t>((k * c.ldb + 4 * nq) * 4));
         else if (MODE == kVecA || MODE == kScalar) rb[r] = load4_scalar(p);
         else if (MODE == kEdge)
             rb[r] = load4_quad(c.B, c.ldb, k0 + k, c.n0 + 4 * nq, c.n0 + 4 * nq < c.N);
@@ -494,18 +520,15 @@ __device__ __forceinline__ void dma16(const float *src, float *dst) {
     __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
 
-// The same through a buffer resource: 16 bytes per lane from base + voff
-// bytes (base wave-uniform, voff < 2^31 per lane; word 3 of the resource,
-// 0x00020000, is the 32-bit data format that gfx9 raw buffer loads take).
-// The per-lane part of the address then stays one 32-bit register for the
+// The same through a buffer resource (buf_rsrc): 16 bytes per lane from
+// base + voff bytes (base wave-uniform, voff < 2^31 per lane).  The per-lane
+// part of the address then stays one 32-bit register for the
 // whole K loop and each slice moves only the uniform base, in scalar
 // registers: the 64-bit vector adds that global loads need per slice
 // competed with the MFMAs (1024^3 6.1%, 512 x 4096 x 4096 6.1% and
 // 1024^2 x 2048 6.7% slower with them).
 __device__ __forceinline__ void dma16b(const float *base, uint32_t voff, float *dst) {
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, 0x7fffffff, 0x00020000);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(buf_rsrc(base), dst, 16, voff, 0, 0, 0);
 }
 
 template <class T>
@@ -1380,7 +1403,11 @@ hipError_t launch_tile(const GemmArgs &a, bool stream_k, void *ws, size_t ws_byt
     Split r = plan_split<T>(a.M, a.N, a.K, stream_k);
     if (workspace_bytes<T>(r) > ws_bytes || (split_wgs(r) > 0 && ws == nullptr))
         return hipErrorInvalidValue;
-    const int vec_a = vec4_ok(a.A, a.lda), vec_b = vec4_ok(a.B, a.ldb);
+    // float4 loads (buffer loads, see fetch) need a lane's byte offset from
+    // the tile's corner below 2^31: rows of A up to 2^31 / (4 BM) floats
+    // apart, rows of B up to 2^31 / (4 BK); farther apart, element loads
+    const int vec_a = vec4_ok(a.A, a.lda) && T::BM * a.lda * 4 <= INT32_MAX;
+    const int vec_b = vec4_ok(a.B, a.ldb) && T::BK * a.ldb * 4 <= INT32_MAX;
     const int vec_c = vec4_ok(a.C, a.ldc);
     const dim3 grid(static_cast<uint32_t>(main_grid<T>(r)));
     hipError_t err;
