@@ -431,6 +431,38 @@ def strided_on_device(x: np.ndarray, ld: int):
     return buf, view
 
 
+# The MFMA rung's full slices load through buffer resources at 32-bit byte
+# offsets from the tile's corner; rows of A 2^23 floats apart (the 64 x 64
+# tile's 64 rows span 2^31 bytes) or rows of B 2^25 apart are beyond that,
+# and those launches load element by element instead.
+@pytest.mark.parametrize("case", ["A_rows", "B_rows"])
+@pytest.mark.parametrize("variant", [tra.MFMA, tra.MFMA_STREAMK, tra.AUTO],
+                         ids=["mfma", "mfma_streamk", "auto"])
+def test_rows_beyond_buffer_offsets(variant, case):
+    import torch
+    M, N, K = (130, 70, 300) if case == "A_rows" else (100, 70, 40)
+    ld = (1 << 23) + 4 if case == "A_rows" else (1 << 25) + 4
+    A, B = int_inputs(M, N, K)
+    ref = oracle.gemm(A, B)
+    log(f"rows beyond buffer offsets: {case} {M}x{N}x{K} ld {ld} variant {variant}")
+    vC = torch.full((M, N), float(C_SENTINEL), dtype=torch.float32, device="cuda:0")
+    if case == "A_rows":
+        buf, v = strided_on_device(A, ld)
+        other = torch.from_numpy(B).to("cuda:0")
+        args = (v.data_ptr(), ld, other.data_ptr(), N, vC.data_ptr(), N)
+    else:
+        buf, v = strided_on_device(B, ld)
+        other = torch.from_numpy(A).to("cuda:0")
+        args = (other.data_ptr(), K, v.data_ptr(), ld, vC.data_ptr(), N)
+    st = tra.gemm_f32_variant(variant, M, N, K, *args, torch.cuda.current_stream().cuda_stream)
+    assert st == tra.TRA_OK, tra.tra_status_string(st)
+    torch.cuda.synchronize()
+    C = vC.cpu().numpy()
+    del buf, v, other, vC
+    torch.cuda.empty_cache()
+    assert_exact(C, ref.c32, f"{case} variant {variant}")
+
+
 @pytest.mark.parametrize("case", ["A_and_C_rows", "B_rows"])
 @pytest.mark.parametrize("variant", RUNGS + [tra.AUTO], ids=RUNG_IDS + ["auto"])
 def test_offsets_past_2_31_elements(variant, case):

@@ -195,6 +195,9 @@ __device__ __forceinline__ float4 load4_elems(const float *X, int64_t ld, int64_
 //   kVecA     A aligned, B not (ldb or the tile's first column not a
 //             multiple of 4): float4 loads of A, element loads of B;
 //   kScalar   element loads of both;
+//             (the MFMA rung loads the quads of all three modes as float4s
+//             through buffer resources, at 4-byte-aligned offsets where
+//             rows are not aligned; the register-blocked rung as written)
 //   kChecked  element loads with zeros outside the matrices: the k tail
 //             slice, and in the register-blocked rung the tiles larger than
 //             the matrix;

@@ -157,17 +157,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const float *base) {
 // base is wave-uniform, so a slice's loads differ only in the scalar base
 // and each lane's 32-bit offset stays fixed over the K loop, where a
 // global load needs a 64-bit vector add per slice beside the MFMAs (4096^3
-// 1.9%, 2048^3 2.2%, 2560^3 2.5% slower).  Element loads keep the global
-// form: four 4-byte buffer loads per quad ran a third slower.
+// 1.9%, 2048^3 2.2%, 2560^3 2.5% slower).  voff need only be a multiple of
+// 4: rows that are not 16-byte aligned load their quads this way too, in
+// place of four element loads (3000 x 2049 x 1531 +4.3%, 1024^2 x 1002
+// +4.8%, 2047 x 1023 x 2047 +4.6%, 4095^3 +2.1%, but 3000^2 x 1002 -3.6%;
+// four 4-byte buffer loads per quad ran a third slower than either).
 __device__ __forceinline__ float4 bload4(const float *base, uint32_t voff) {
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(base), voff, 0, 0);
     return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
                        __uint_as_float(v.w));
 }
 
-// Loads slice k0 .. k0+BK of the A and B tiles into registers.  The float4
-// modes take byte offsets from the tile's corner below 2^31 (vec_a and vec_b
-// are set only then, see launch_tile).
+// Loads slice k0 .. k0+BK of the A and B tiles into registers.  The full-
+// slice modes (kVec, kVecA, kScalar) load through buffer resources at byte
+// offsets from the tile's corner, which tile_pass makes sure stay below
+// 2^31.
 template <class T, int MODE>
 __device__ __forceinline__ void fetch(const Ctx<T> &c, int64_t k0, float4 (&ra)[T::A_F4],
                                       float4 (&rb)[T::B_F4]) {
@@ -177,11 +181,9 @@ __device__ __forceinline__ void fetch(const Ctx<T> &c, int64_t k0, float4 (&ra)[
         if (T::A_VEC % T::THREADS != 0 && f >= T::A_VEC) break;
         int m, kq;
         a_quad_of<T>(f, m, kq);
-        const float *p = c.A + (c.m0 + m) * c.lda + k0 + 4 * kq;
-        if (MODE == kVec || MODE == kVecA)
+        if (MODE == kVec || MODE == kVecA || MODE == kScalar)
             ra[r] = bload4(c.A + c.m0 * c.lda + k0,
                            static_cast<uint32_t>((m * c.lda + 4 * kq) * 4));
-        else if (MODE == kScalar) ra[r] = load4_scalar(p);
         else if (MODE == kEdge)
             ra[r] = load4_quad(c.A, c.lda, c.m0 + m, k0 + 4 * kq, c.m0 + m < c.M);
         else if (MODE == kEdgeElem)
@@ -193,11 +195,9 @@ __device__ __forceinline__ void fetch(const Ctx<T> &c, int64_t k0, float4 (&ra)[
         const int f = c.t + T::THREADS * r;
         if (T::B_VEC % T::THREADS != 0 && f >= T::B_VEC) break;
         const int k = f / (T::BN / 4), nq = f % (T::BN / 4);
-        const float *p = c.B + (k0 + k) * c.ldb + c.n0 + 4 * nq;
-        if (MODE == kVec)
+        if (MODE == kVec || MODE == kVecA || MODE == kScalar)
             rb[r] = bload4(c.B + k0 * c.ldb + c.n0,
                            static_cast<uint32_t>((k * c.ldb + 4 * nq) * 4));
-        else if (MODE == kVecA || MODE == kScalar) rb[r] = load4_scalar(p);
         else if (MODE == kEdge)
             rb[r] = load4_quad(c.B, c.ldb, k0 + k, c.n0 + 4 * nq, c.n0 + 4 * nq < c.N);
         else if (MODE == kEdgeElem)
@@ -298,7 +298,7 @@ __device__ __forceinline__ void il_order() {
     constexpr int SECOND = NM - NM / 2 > 0 ? NM - NM / 2 : 1;
     constexpr int NDR = T::FM * (T::HALF / 4) + (T::HALF * T::FN + 1) / 2;
     constexpr int NDW = T::A_F4 + T::B_F4;
-    constexpr int NVM = (MODE == kVec || MODE == kEdge ? 1 : 4) * (T::A_F4 + T::B_F4);
+    constexpr int NVM = (MODE == kEdgeElem || MODE == kChecked ? 4 : 1) * (T::A_F4 + T::B_F4);
     il_schedule<0, NM, (NDR + FIRST - 1) / FIRST, (NDW + SECOND - 1) / SECOND,
                 (NVM + SECOND - 1) / SECOND>();
 }
@@ -851,9 +851,14 @@ __device__ __forceinline__ void tile_pass(const Ctx<T> &c, int vec_a, int vec_b,
         // float4s when its rows are aligned and N is a multiple of 4 (then
         // so is n0, and a quad is wholly inside or outside)
         const bool quads = vec_a && vec_b && (c.N & 3) == 0 && (c.n0 & 3) == 0;
+        // kVec, kVecA and kScalar load through buffer resources at byte
+        // offsets from the tile's corner, below 2^31 only while rows of A
+        // are fewer than 2^31 / (4 BM) floats apart and rows of B fewer
+        // than 2^31 / (4 BK); farther apart, the element loads of kEdgeElem
+        const bool bufok = BM * c.lda * 4 <= INT32_MAX && T::BK * c.ldb * 4 <= INT32_MAX;
         if (!inside && quads)
             k_loop<T, kEdge>(c, lds, wm0 + l32, wn0 + l32, kbase, acc, s0, n);
-        else if (!inside)
+        else if (!inside || !bufok)
             k_loop<T, kEdgeElem>(c, lds, wm0 + l32, wn0 + l32, kbase, acc, s0, n);
         else if (vec_a && vec_b && (c.n0 & 3) == 0)
             k_loop<T, kVec>(c, lds, wm0 + l32, wn0 + l32, kbase, acc, s0, n);
