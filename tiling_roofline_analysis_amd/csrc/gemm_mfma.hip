@@ -45,7 +45,7 @@
 // Direct staging (k_loop_dma): where every load is an aligned float4 inside
 // the matrices and K is a multiple of 4 -- the common case of contiguous
 // operands -- the 64 x 64 tiles move their slices from global memory
-// straight into a ring of S LDS stages (global_load_lds_dwordx4), with no
+// straight into a ring of S LDS stages (buffer_load_dwordx4 ... lds), with no
 // register sets and no LDS stores; the slice that runs past K, if any,
 // reads a zero word for the quads past K.  The layout and the waits are
 // described at Dma below.
@@ -425,9 +425,10 @@ __device__ __forceinline__ void k_loop(const Ctx<T> &c, float *lds, int arow, in
 
 // ---- direct staging: global memory to LDS without registers ----
 //
-// gfx950's global_load_lds_dwordx4 writes 16 bytes per lane straight into
-// LDS, lane i of a wave at byte 16 i past a wave-uniform base (M0): the
-// data lands in no register, needs no ds_write and no wait before one.
+// gfx950's 16-byte loads into LDS (global_load_lds_dwordx4, and the buffer
+// form used by dma16b) write 16 bytes per lane straight into LDS, lane i
+// of a wave at byte 16 i past a wave-uniform base (M0): the data lands in
+// no register, needs no ds_write and no wait before one.
 // Each instruction moves 1 KB per wave, so a slice is laid out in 1 KB
 // blocks:
 //   A block: 16 rows of the slice, 4 quads a row (rows 16 words apart);
