@@ -337,6 +337,9 @@ def test_caller_workspace_checked_on_host():
     ((2688, 2752, 1000), "mfma"),          # 1806 tiles: 13.4% uneven, but in stream-K runs
     ((3500, 3500, 1500), "mfma"),          # 3025 tiles: 11.82 a CU, 1.6% uneven
     ((5000, 5000, 1000), "mfma_streamk"),  # 800 tiles of 256 x 128: 3.13 a CU
+    ((5880, 3806, 5236), "mfma_streamk"),  # 690 tiles of 256 x 128: 11.3% uneven (runs)
+    ((6144, 3840, 4096), "mfma"),          # 720 tiles of 256 x 128: 6.7% uneven
+    ((2560, 3072, 2048), "mfma"),          # 480 tiles of 128 x 128: 6.7% uneven
     ((8192, 64, 2048), "mfma_streamk"),    # 128 tiles: exactly half the CUs
     ((4096, 128, 2048), "mfma_streamk"),   # 128 tiles
     ((12288, 64, 2048), "mfma"),           # 192 tiles of 128 slices: saves < 8 us

@@ -1522,7 +1522,12 @@ bool stream_k_pays(int64_t M, int64_t N, int64_t K) {
         return false;
     const double over = static_cast<double>(ceil_div(tiles, cus) * cus) /
                         static_cast<double>(tiles) - 1.0;
-    return over >= (r.pp.parts > 0 ? 0.10 : (T::THREADS == 512 ? 0.15 : 0.25));
+    // runs: 10% on the 256 x 128 tile (5880 x 3806 x 4096 +6.8%, 5659 x 4937
+    // x 4096 +10.9% at 11% and 14%; +0.4 to +4.5% at 6-7%), 15% on the
+    // 128 x 128 tile (at 7% and K = 2048 the runs lost 4-5%), 25% on the
+    // 64 x 64 tiles
+    const double runs = T::BM == 256 ? 0.10 : (T::THREADS == 512 ? 0.15 : 0.25);
+    return over >= (r.pp.parts > 0 ? 0.10 : runs);
 }
 
 bool prefer_stream_k(int64_t M, int64_t N, int64_t K) {
