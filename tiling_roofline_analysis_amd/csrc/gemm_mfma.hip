@@ -1495,10 +1495,11 @@ LaunchPlan plan_mfma(int64_t M, int64_t N, int64_t K, bool stream_k) {
 //     200x300x4100: 20 tiles, 65 -> 18 us; 8192x64x2048: 128 tiles, 34 ->
 //     29 us; not 768x768x1024: 144 tiles, 19 against 22 us);
 //   * otherwise when one tile per workgroup would leave some CUs a whole
-//     tile more work than the mean by at least 10% (split in parts), or by
-//     at least 15% (8-wave tiles) or 25% (4-wave tiles) in stream-K runs,
-//     which need a launch of their own, and the product is large enough
-//     (>= 4 GFLOP) to hide the second launch.  Measured on 64 x 64 tiles:
+//     tile more work than the mean by at least 10% (split in parts), or in
+//     stream-K runs, which need a launch of their own, by at least 10%
+//     (256 x 128 tile), 15% (128 x 128) or 25% (64 x 64), and the product
+//     is large enough (>= 4 GFLOP) to hide the second launch.  Measured on
+//     64 x 64 tiles:
 //     parts at 3-8% above the mean lost 0-3%, at 10.8%, 11.6% and 15.5%
 //     (3000x2049x1531) gained 2%, 3% and 5%; runs at 5-15% ranged from -5%
 //     to +3%, at 18.5% (2304^2 x 1000) lost 14% and at 58% (1152^2 x 8192)
