@@ -361,6 +361,18 @@ def test_auto_choice(shape, rung):
     ((2000, 2600, 3000), "<128x128x16, 8 waves>"),          # 336 tiles, edges wasted no worse
     ((3000, 3000, 1000), "<64x64x16, 4 waves, 6 LDS stages>"),     # short K stays on 64x64
     ((3072, 3072, 3072), "<64x64x16, 4 waves, 6 LDS stages>"),     # 576 tiles: 2.25 a CU
+    # 256 tiles of 128x128 or 256x128 whose columns or rows lie half or
+    # more outside the matrix: 64x64 tiles instead
+    ((32768, 64, 8192), "<64x64x16, 4 waves, 6 LDS stages>"),
+    ((65536, 64, 1024), "<64x64x16, 4 waves, 6 LDS stages>"),
+    ((64, 65536, 4096), "<64x64x16, 4 waves, 6 LDS stages>"),
+    ((384, 16384, 4096), "<128x128x16, 8 waves>"),  # not 256x128: a quarter outside
+    ((2049, 32768, 1024), "<64x64x16, 4 waves, 6 LDS stages>"),
+    ((32768, 32, 4096), "<64x64x16, 4 waves, 4 sets>"),            # N < 64: no direct loads
+    # the larger tiles where they waste no more of the edges
+    ((65536, 128, 2048), "<256x128x16, 8 waves, 4 sets>"),
+    ((32768, 128, 4096), "<128x128x16, 8 waves>"),
+    ((4000, 4200, 203), "<256x128x16, 8 waves, 4 sets>"),
 ])
 def test_auto_tile_class(shape, tile):
     d = tra.tra_gemm_describe(tra.AUTO, *shape)

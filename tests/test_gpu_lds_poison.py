@@ -49,6 +49,8 @@ SHAPES = [
     (1000, 1000, 1000),   # direct loads, the last slice past K
     (700, 900, 1548),     # direct loads, the last slice past K
     (300, 500, 260),      # direct loads, the last slice past K, 17 slices
+    (16384, 64, 4112),    # direct loads, one column of tiles, long K
+    (16384, 64, 4100),    # the same, the last slice past K
 ]
 
 

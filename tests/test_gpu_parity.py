@@ -315,6 +315,9 @@ DMA_SHAPES = [
     (1000, 1000, 212, _DMA),      # R = 8
     (300, 500, 244, _DMA),        # R = 10
     (300, 500, 260, _DMA),        # R = 11
+    (16384, 64, 4112, _DMA),      # one column of tiles, A 270 MB; R = 11
+    (16384, 64, 4100, _DMA),      # 4 of the last slice's 16 k inside, R = 11
+    (32768, 64, 1024, _DMA),      # 512 tiles in one column (128 x 128 tiles would be half outside)
 ]
 
 

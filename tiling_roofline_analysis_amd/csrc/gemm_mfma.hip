@@ -1197,17 +1197,27 @@ Shape pick(int64_t M, int64_t N, int64_t K) {
     const int64_t cus = kMi355xCUs;
     const int64_t tiles128 = ceil_div(M, 128) * ceil_div(N, 128);
     const int64_t large = ceil_div(M, 256) * ceil_div(N, 128);
+    // The larger tiles only where they waste no more of the edges than
+    // 64x64 tiles (at most 3% more of the tile grid outside M x N): with
+    // N = 64 half of every 128-wide tile lies outside the matrix, with
+    // M = 64 three quarters of every 256-high one.  Against the larger
+    // tiles: 32768x64x8192 517 -> 289 us, 64x65536x4096 973 -> 320,
+    // 128x65536x2048 497 -> 277, 16384x192x4096 237 -> 191, 384x16384x4096
+    // 462 -> 362, 640x32768x2048 704 -> 612, 2049x32768x1024 1075 -> 1000,
+    // 2049x8192x4096 1046 -> 1000, 65536x300x2048 711 -> 665.
+    const double c64 = cover(M, N, 64, 64);
+    const bool fit256 = cover(M, N, 256, 128) >= 0.97 * c64;
+    const bool fit128 = cover(M, N, 128, 128) >= 0.97 * c64;
     // Large: about 4 tiles of 128x128 per CU, or a whole number of 256x128
     // tiles per CU (4096x2048x1024: 135 -> 126 us against 64x64 tiles)
-    if (tiles128 >= 4 * cus || (large >= cus && large % cus == 0)) return Shape::kLarge;
-    if (4 * tiles128 > 3 * cus && tiles128 <= cus) return Shape::kMid;
+    if (fit256 && (tiles128 >= 4 * cus || (large >= cus && large % cus == 0)))
+        return Shape::kLarge;
+    if (fit128 && 4 * tiles128 > 3 * cus && tiles128 <= cus) return Shape::kMid;
     // Mid also for one to two 128x128 tiles per CU once K is long enough to
     // pay for the stream-K split that evens them out, unless 128x128 tiles
     // waste more of the edges (3000x2049x1531 stays on 64x64 tiles):
     // 2304^3 207 -> 193 us, 1536x4096x4096 386 -> 382 us
-    if (tiles128 > cus && tiles128 < 2 * cus && K >= 2048 &&
-        cover(M, N, 128, 128) >= 0.97 * cover(M, N, 64, 64))
-        return Shape::kMid;
+    if (fit128 && tiles128 > cus && tiles128 < 2 * cus && K >= 2048) return Shape::kMid;
     return K > 1024 ? Shape::kDeep : Shape::kMany;
 }
 
