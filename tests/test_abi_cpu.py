@@ -369,10 +369,15 @@ def test_auto_choice(shape, rung):
     ((384, 16384, 4096), "<128x128x16, 8 waves>"),  # not 256x128: a quarter outside
     ((2049, 32768, 1024), "<64x64x16, 4 waves, 6 LDS stages>"),
     ((32768, 32, 4096), "<64x64x16, 4 waves, 4 sets>"),            # N < 64: no direct loads
+    # K of at most 16 slices and M >= 2048: several 64x64 tiles a CU
+    ((4096, 4096, 256), "<64x64x16, 4 waves, 6 LDS stages>"),
+    ((4096, 4096, 128), "<64x64x16, 4 waves>"),             # under 13 slices: register-staged
+    ((4096, 4096, 512), "<256x128x16, 8 waves, 4 sets>"),
+    ((1000, 4096, 256), "<128x128x16, 8 waves>"),
     # the larger tiles where they waste no more of the edges
     ((65536, 128, 2048), "<256x128x16, 8 waves, 4 sets>"),
     ((32768, 128, 4096), "<128x128x16, 8 waves>"),
-    ((4000, 4200, 203), "<256x128x16, 8 waves, 4 sets>"),
+    ((4000, 4200, 259), "<256x128x16, 8 waves, 4 sets>"),
 ])
 def test_auto_tile_class(shape, tile):
     d = tra.tra_gemm_describe(tra.AUTO, *shape)

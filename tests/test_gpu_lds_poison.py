@@ -30,7 +30,7 @@ SHAPES = [
     (200, 300, 4100),     # few tiles, long K
     (700, 900, 1500),     # 64 x 64, four register sets
     (1900, 2000, 300),    # 128 x 128 tiles
-    (4000, 4200, 203),    # 256 x 128 tiles, every edge ragged
+    (4000, 4200, 259),    # 256 x 128 tiles, every edge ragged
     (2040, 4090, 300),    # 256 tiles of 256 x 128
     (2000, 2600, 2050),   # 128 x 128 with stream-K
     (3000, 2049, 1531),   # the ragged configuration

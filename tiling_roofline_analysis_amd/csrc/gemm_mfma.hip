@@ -1205,6 +1205,15 @@ Shape pick(int64_t M, int64_t N, int64_t K) {
     // 128x65536x2048 497 -> 277, 16384x192x4096 237 -> 191, 384x16384x4096
     // 462 -> 362, 640x32768x2048 704 -> 612, 2049x32768x1024 1075 -> 1000,
     // 2049x8192x4096 1046 -> 1000, 65536x300x2048 711 -> 665.
+    // Short K (at most 16 slices) with M >= 2048: 64x64 tiles, several a CU,
+    // so that one tile's first loads and stores overlap another's MFMAs;
+    // on a single larger tile per CU they do not (4096^2 x 128 47.1 -> 42.8
+    // us, 2048x4096x128 25.9 -> 23.1, 4096^2 x 224 66.5 -> 62.6, 6144^2 x
+    // 256 179 -> 155, 16384^2 x 256 1166 -> 1119, 2048^2 x 256 21.2 ->
+    // 19.7, 16384x4096x256 285 -> 279).  Not with K = 512 (2048^2 x 512
+    // 35.6 -> 40.7 us) nor for smaller M (1000x4096x256 21.7 -> 23.9,
+    // 500x8192x256 21.8 -> 24.0; 1024x4096x256 gained, 21.1 -> 19.8).
+    if (K <= 256 && M >= 2048) return Shape::kMany;
     const double c64 = cover(M, N, 64, 64);
     const bool fit256 = cover(M, N, 256, 128) >= 0.97 * c64;
     const bool fit128 = cover(M, N, 128, 128) >= 0.97 * c64;
