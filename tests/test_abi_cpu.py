@@ -336,7 +336,7 @@ def test_caller_workspace_checked_on_host():
     ((2560, 3328, 1000), "mfma_streamk"),  # 2080 tiles: 8.13 a CU, 10.8% uneven (parts)
     ((2688, 2752, 1000), "mfma"),          # 1806 tiles: 13.4% uneven, but in stream-K runs
     ((3500, 3500, 1500), "mfma"),          # 3025 tiles: 11.82 a CU, 1.6% uneven
-    ((5000, 5000, 1000), "mfma_streamk"),  # 800 tiles of 256 x 128: 3.13 a CU
+    ((5000, 5000, 1000), "mfma"),          # 800 tiles of 256 x 128 would be 3.13 a CU: 64 x 64 instead
     ((5880, 3806, 5236), "mfma_streamk"),  # 690 tiles of 256 x 128: 11.3% uneven (runs)
     ((6144, 3840, 4096), "mfma"),          # 720 tiles of 256 x 128: 6.7% uneven
     ((2560, 3072, 2048), "mfma"),          # 480 tiles of 128 x 128: 6.7% uneven
@@ -374,10 +374,15 @@ def test_auto_choice(shape, rung):
     ((4096, 4096, 128), "<64x64x16, 4 waves>"),             # under 13 slices: register-staged
     ((4096, 4096, 512), "<256x128x16, 8 waves, 4 sets>"),
     ((1000, 4096, 256), "<128x128x16, 8 waves>"),
+    # K <= 1024 and 256x128 tiles that leave a partial last wave: 64x64
+    ((4608, 4608, 512), "<64x64x16, 4 waves, 6 LDS stages>"),    # 648 tiles, 2.53 a CU
+    ((6144, 6144, 1024), "<64x64x16, 4 waves, 6 LDS stages>"),   # 1152 tiles, 4.5 a CU
+    ((6144, 6144, 2048), "<256x128x16, 8 waves, 4 sets>"),       # longer K: split in parts
+    ((8192, 6144, 512), "<256x128x16, 8 waves, 4 sets>"),        # 1536 tiles, 6 a CU
     # the larger tiles where they waste no more of the edges
     ((65536, 128, 2048), "<256x128x16, 8 waves, 4 sets>"),
     ((32768, 128, 4096), "<128x128x16, 8 waves>"),
-    ((4000, 4200, 259), "<256x128x16, 8 waves, 4 sets>"),
+    ((4000, 4200, 1027), "<256x128x16, 8 waves, 4 sets>"),
 ])
 def test_auto_tile_class(shape, tile):
     d = tra.tra_gemm_describe(tra.AUTO, *shape)

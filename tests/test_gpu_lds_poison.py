@@ -30,14 +30,14 @@ SHAPES = [
     (200, 300, 4100),     # few tiles, long K
     (700, 900, 1500),     # 64 x 64, four register sets
     (1900, 2000, 300),    # 128 x 128 tiles
-    (4000, 4200, 259),    # 256 x 128 tiles, every edge ragged
+    (4000, 4200, 1027),    # 256 x 128 tiles, every edge ragged
     (2040, 4090, 300),    # 256 tiles of 256 x 128
     (2000, 2600, 2050),   # 128 x 128 with stream-K
     (3000, 2049, 1531),   # the ragged configuration
     (3000, 32, 1100),     # narrower than a tile: float4 loads, column quads past N zeroed
     (40, 2000, 700),      # shorter than a tile: float4 loads, rows past M zeroed
     (3000, 33, 1100),     # narrower than a tile, N odd: element loads
-    (200, 66000, 40),     # 256 x 128 tiles taller than M
+    (200, 65500, 40),     # 256 x 128 tiles taller than M
     (1000, 1000, 1007),   # register-blocked rung: K split over 3 lane groups, K tail
     (300, 700, 255),      # register-blocked rung: K split over 4 lane groups
     (100, 200, 127),      # register-blocked rung: K split over 2 lane groups

@@ -253,7 +253,7 @@ def test_edge_sizes_all_pairs(variant):
 # 64 x 64 tiles would otherwise load directly into LDS): (M, N, K, expected
 # tile).
 MFMA_TILE_SHAPES = [
-    (4000, 4200, 259, "<256x128x16, 8 waves, 4 sets>"),   # 16 x 33 = 528 tiles of 256 x 128
+    (4000, 4200, 1027, "<256x128x16, 8 waves, 4 sets>"),   # 16 x 33 = 528 tiles of 256 x 128
     (1900, 2000, 300, "<128x128x16, 8 waves>"),   # 15 x 16 = 240 tiles of 128 x 128
     (1500, 1500, 77, "<64x64x16, 4 waves>"),      # 576 tiles of 64 x 64, short K
     (200, 300, 4101, "<64x64x16, 4 waves, 4 sets>"),   # few tiles, long K
@@ -264,7 +264,7 @@ MFMA_TILE_SHAPES = [
     (3000, 32, 1100, "<64x64x16, 4 waves, 4 sets>"),   # narrower than a tile (float4 loads)
     (40, 2000, 700, "<64x64x16, 4 waves>"),       # shorter than a tile (float4 loads)
     (3000, 33, 1100, "<64x64x16, 4 waves, 4 sets>"),   # narrower than a tile, N odd
-    (200, 66000, 40, "<256x128x16, 8 waves, 4 sets>"),   # large tiles taller than M
+    (200, 65500, 40, "<256x128x16, 8 waves, 4 sets>"),   # large tiles taller than M
     (100, 30001, 40, "<128x128x16, 8 waves>"),    # 128 x 128 tiles taller than M, N odd
 ]
 
@@ -392,7 +392,7 @@ def stride_case(M, N, K):
 
 
 @pytest.mark.parametrize("layout", ["padded_aligned", "padded_misaligned"])
-@pytest.mark.parametrize("shape", [(300, 200, 150), (4000, 4200, 259), (1500, 1500, 77),
+@pytest.mark.parametrize("shape", [(300, 200, 150), (4000, 4200, 1027), (1500, 1500, 77),
                                    (50, 36, 300)],
                          ids=lambda s: f"{s[0]}x{s[1]}x{s[2]}")
 @pytest.mark.parametrize("variant", RUNGS, ids=RUNG_IDS)

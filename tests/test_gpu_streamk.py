@@ -42,7 +42,7 @@ SPLIT_SHAPES = [
     (300, 500, 203, "parts"),     # all 40 tiles in 6 parts of 2-3 slices
     (257, 129, 1000, "parts"),    # all 15 tiles in 8 parts
     (3000, 2049, 1531, "parts"),  # the ragged shape: its last 15 tiles in 8 parts
-    (4000, 4200, 259, "parts"),   # 528 tiles of 256 x 128: the last 16 in 8 parts
+    (4000, 4200, 1027, "parts"),   # 528 tiles of 256 x 128: the last 16 in 8 parts
     (1500, 1500, 77, "runs"),     # 576 tiles of 64 x 64 in under a wave, 5 slices each
     (1152, 1152, 8192, "runs"),   # 324 tiles: 2 parts each would leave CUs uneven
     (4608, 4608, 4096, "runs"),   # 648 tiles of 256 x 128: the last 136, over half a wave
@@ -112,7 +112,7 @@ def test_caller_workspace_matches_library_workspace():
 
 def test_library_workspace_grows_and_serves_several_streams():
     import torch
-    small, large = (300, 500, 203), (4000, 4200, 259)
+    small, large = (300, 500, 203), (4000, 4200, 1027)
     assert (tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, *small)
             < tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, *large))
     cases = {}
@@ -152,7 +152,7 @@ def test_threads_on_their_own_streams_share_the_library_safely():
     # bit for bit (the split's reduction order is fixed)
     import threading
     import torch
-    shapes = [(4000, 4200, 259), (1500, 1500, 77)]
+    shapes = [(4000, 4200, 1027), (1500, 1500, 77)]
     assert (tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, *shapes[0])
             < tra.tra_gemm_workspace_size(tra.MFMA_STREAMK, *shapes[1]))
     operands, expect = {}, {}
@@ -215,7 +215,7 @@ def test_streams_destroyed_and_recreated_between_split_calls():
     import ctypes
     import torch
     hip = _hip_runtime()
-    small, large = (300, 500, 203), (4000, 4200, 259)
+    small, large = (300, 500, 203), (4000, 4200, 1027)
     cases = {s: _int_case(*s) for s in (small, large)}
     handles = []
     for i, shape in enumerate((small, large, small, large, large, small)):
@@ -244,7 +244,7 @@ def test_per_thread_default_stream_keeps_one_workspace_per_thread():
     import torch
     hip = _hip_runtime()
     per_thread = 2   # hipStreamPerThread
-    shapes = [(300, 500, 203), (4000, 4200, 259)]
+    shapes = [(300, 500, 203), (4000, 4200, 1027)]
     cases = {s: _int_case(*s) for s in shapes}
     outs = {(t, i): torch.full(shapes[(t + i) % 2][:2], float("nan"), device="cuda:0")
             for t in range(4) for i in range(4)}

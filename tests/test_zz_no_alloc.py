@@ -49,7 +49,7 @@ def both(variant, M, N, K, A, B):
 # (first, second) shapes: the second is smaller; the forms of the split
 PAIRS = [
     ((3000, 2049, 1531), (300, 500, 203), "parts", "parts"),
-    ((4000, 4200, 259), (1500, 1500, 77), "parts", "runs"),
+    ((4000, 4200, 1027), (1500, 1500, 77), "parts", "runs"),
     ((1152, 1152, 8192), (257, 129, 1000), "runs", "parts"),
 ]
 

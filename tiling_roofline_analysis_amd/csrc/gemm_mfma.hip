@@ -1217,9 +1217,18 @@ Shape pick(int64_t M, int64_t N, int64_t K) {
     const double c64 = cover(M, N, 64, 64);
     const bool fit256 = cover(M, N, 256, 128) >= 0.97 * c64;
     const bool fit128 = cover(M, N, 128, 128) >= 0.97 * c64;
+    // With K <= 1024, only when the 256x128 tiles fill the CUs to within 5%
+    // of whole waves: the split that evens out a partial last wave does not
+    // pay for itself on so few slices, and the 64x64 tiles, many a CU, are
+    // even by themselves (against 256x128 tiles split in parts or runs:
+    // 4608^2 x 512 195 -> 165 us, 3072x6144x512 162 -> 145, 4608^2 x 1024
+    // 337 -> 313, 6144x3072x1024 289 -> 272, 6144^2 x 512 303 -> 285,
+    // 6144^2 x 1024 558 -> 541, 7168^2 x 1024 756 -> 732; with K = 2048
+    // the split forms were within 1.4%)
+    const bool even256 = K > 1024 || 20 * large >= 19 * ceil_div(large, cus) * cus;
     // Large: about 4 tiles of 128x128 per CU, or a whole number of 256x128
     // tiles per CU (4096x2048x1024: 135 -> 126 us against 64x64 tiles)
-    if (fit256 && (tiles128 >= 4 * cus || (large >= cus && large % cus == 0)))
+    if (fit256 && even256 && (tiles128 >= 4 * cus || (large >= cus && large % cus == 0)))
         return Shape::kLarge;
     if (fit128 && 4 * tiles128 > 3 * cus && tiles128 <= cus) return Shape::kMid;
     // Mid also for one to two 128x128 tiles per CU once K is long enough to
