@@ -1532,7 +1532,8 @@ LaunchPlan plan_mfma(int64_t M, int64_t N, int64_t K, bool stream_k) {
 //     (3000x2049x1531) gained 2%, 3% and 5%; runs at 5-15% ranged from -5%
 //     to +3%, at 18.5% (2304^2 x 1000) lost 14% and at 58% (1152^2 x 8192)
 //     gained 20%.  On the 8-wave tiles, one workgroup a CU: parts at 11%
-//     (6144^2 x 1024) +6%, 28% (5000^2 x 1000) +21%; runs at 18.5%
+//     (6144^2 x 1024) +6%, 28% (5000^2 x 1000) +21% (both now take 64x64
+//     tiles, see pick); runs at 18.5%
 //     (4608^2 x 4096) +11%, 28% (2560^3) +12%.
 template <class T>
 bool stream_k_pays(int64_t M, int64_t N, int64_t K) {
