@@ -379,6 +379,9 @@ def test_auto_choice(shape, rung):
     ((6144, 6144, 1024), "<64x64x16, 4 waves, 6 LDS stages>"),   # 1152 tiles, 4.5 a CU
     ((6144, 6144, 2048), "<256x128x16, 8 waves, 4 sets>"),       # longer K: split in parts
     ((8192, 6144, 512), "<256x128x16, 8 waves, 4 sets>"),        # 1536 tiles, 6 a CU
+    # exactly three 128x128 tiles a CU, K >= 2048
+    ((2048, 6144, 4096), "<128x128x16, 8 waves>"),
+    ((2048, 6144, 1024), "<64x64x16, 4 waves, 6 LDS stages>"),
     # the larger tiles where they waste no more of the edges
     ((65536, 128, 2048), "<256x128x16, 8 waves, 4 sets>"),
     ((32768, 128, 4096), "<128x128x16, 8 waves>"),

@@ -1236,6 +1236,11 @@ Shape pick(int64_t M, int64_t N, int64_t K) {
     // waste more of the edges (3000x2049x1531 stays on 64x64 tiles):
     // 2304^3 207 -> 193 us, 1536x4096x4096 386 -> 382 us
     if (fit128 && tiles128 > cus && tiles128 < 2 * cus && K >= 2048) return Shape::kMid;
+    // and for exactly three 128x128 tiles per CU, which leave no partial
+    // wave (2048x6144x4096 710 -> 695 us, 3072x4096x8192 1419 -> 1379,
+    // 6144x2048x3072 537 -> 525, 2048x6144x2048 +0.9%; within 2% either
+    // way with K <= 1024)
+    if (fit128 && tiles128 == 3 * cus && K >= 2048) return Shape::kMid;
     return K > 1024 ? Shape::kDeep : Shape::kMany;
 }
 
