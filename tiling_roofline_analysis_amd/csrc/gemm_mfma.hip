@@ -1197,14 +1197,6 @@ Shape pick(int64_t M, int64_t N, int64_t K) {
     const int64_t cus = kMi355xCUs;
     const int64_t tiles128 = ceil_div(M, 128) * ceil_div(N, 128);
     const int64_t large = ceil_div(M, 256) * ceil_div(N, 128);
-    // The larger tiles only where they waste no more of the edges than
-    // 64x64 tiles (at most 3% more of the tile grid outside M x N): with
-    // N = 64 half of every 128-wide tile lies outside the matrix, with
-    // M = 64 three quarters of every 256-high one.  Against the larger
-    // tiles: 32768x64x8192 517 -> 289 us, 64x65536x4096 973 -> 320,
-    // 128x65536x2048 497 -> 277, 16384x192x4096 237 -> 191, 384x16384x4096
-    // 462 -> 362, 640x32768x2048 704 -> 612, 2049x32768x1024 1075 -> 1000,
-    // 2049x8192x4096 1046 -> 1000, 65536x300x2048 711 -> 665.
     // Short K (at most 16 slices) with M >= 2048: 64x64 tiles, several a CU,
     // so that one tile's first loads and stores overlap another's MFMAs;
     // on a single larger tile per CU they do not (4096^2 x 128 47.1 -> 42.8
@@ -1214,6 +1206,14 @@ Shape pick(int64_t M, int64_t N, int64_t K) {
     // 35.6 -> 40.7 us) nor for smaller M (1000x4096x256 21.7 -> 23.9,
     // 500x8192x256 21.8 -> 24.0; 1024x4096x256 gained, 21.1 -> 19.8).
     if (K <= 256 && M >= 2048) return Shape::kMany;
+    // The larger tiles only where they waste no more of the edges than
+    // 64x64 tiles (at most 3% more of the tile grid outside M x N): with
+    // N = 64 half of every 128-wide tile lies outside the matrix, with
+    // M = 64 three quarters of every 256-high one.  Against the larger
+    // tiles: 32768x64x8192 517 -> 289 us, 64x65536x4096 973 -> 320,
+    // 128x65536x2048 497 -> 277, 16384x192x4096 237 -> 191, 384x16384x4096
+    // 462 -> 362, 640x32768x2048 704 -> 612, 2049x32768x1024 1075 -> 1000,
+    // 2049x8192x4096 1046 -> 1000, 65536x300x2048 711 -> 665.
     const double c64 = cover(M, N, 64, 64);
     const bool fit256 = cover(M, N, 256, 128) >= 0.97 * c64;
     const bool fit128 = cover(M, N, 128, 128) >= 0.97 * c64;
