@@ -687,14 +687,56 @@ def test_non_finite_inputs_propagate(variant, shape):
 def _random_large_shapes(seed, n):
     # sides drawn around each tile class's range: 64 x 64 tiles (900-3000),
     # 128 x 128 tiles (about one per CU, 1750-2050) and 256 x 128 tiles
-    # (at least 4 of 128 x 128 per CU, 4100-4700)
+    # (at least 4 of 128 x 128 per CU, 4100-4700; K above 1024, where they
+    # are taken also when they leave a partial last wave)
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
         lo, hi = [(900, 3000), (1750, 2050), (4100, 4700)][i % 3]
+        klo, khi = (1030, 1500) if i % 3 == 2 else (40, 700)
         out.append((int(rng.integers(lo, hi)), int(rng.integers(lo, hi)),
-                    int(rng.integers(40, 700))))
+                    int(rng.integers(klo, khi))))
     return out
+
+
+def _picker_route_shapes(seed):
+    # seeded shapes on each route of the tile-class choice, with the tile
+    # each must take: short K with M >= 2048 (64 x 64); 256 x 128 tiles that
+    # would leave a partial last wave with K <= 1024 (64 x 64); the same
+    # with K > 1024 (256 x 128, split); exactly three 128 x 128 tiles a CU
+    # with K >= 2048 (128 x 128); N of 64 to 70 under tall M, where wider
+    # tiles would lie half outside (64 x 64)
+    rng = np.random.default_rng(seed)
+    r = lambda lo, hi: int(rng.integers(lo, hi))
+    out = []
+    for _ in range(2):
+        out += [((r(2048, 5000), r(1000, 5000), r(40, 257)), "64x64x16"),
+                ((r(4300, 4700), r(4300, 4700), r(300, 1025)), "64x64x16"),
+                ((r(4300, 4700), r(4300, 4700), r(1100, 1400)), "256x128x16"),
+                ((r(1985, 2049), r(6081, 6145), r(2048, 2300)), "128x128x16"),
+                ((r(20000, 33000), r(64, 71), r(100, 400)), "64x64x16")]
+    return out
+
+
+@pytest.mark.parametrize("variant", [tra.AUTO, tra.MFMA, tra.MFMA_STREAMK],
+                         ids=["auto", "mfma", "mfma_streamk"])
+def test_picker_routes_int_patterns_exact(variant):
+    """Seeded shapes on every route of the tile-class choice take the tile
+    that route names, and every element matches the oracle's values on one
+    period of the integer patterns (13 x 7), plus a direct sample."""
+    for (M, N, K), tile in _picker_route_shapes(23):
+        d = tra.tra_gemm_describe(variant, M, N, K)
+        log(f"[case] picker route {tra.tra_gemm_variant_name(variant)} {M}x{N}x{K} ({d})")
+        assert f"tile={tile} " in d, (M, N, K, d)
+        A, B = int_inputs(M, N, K)
+        C, *_ = run_gpu(variant, A, B)
+        ii, jj = np.meshgrid(np.arange(13), np.arange(7), indexing="ij")
+        T = oracle.gemm_entries(A, B, ii.ravel(), jj.ravel()).c32.reshape(ii.shape)
+        assert_exact(C, T[np.arange(M)[:, None] % 13, np.arange(N)[None, :] % 7],
+                     f"{M}x{N}x{K}")
+        rows, cols = sample_entries(M, N, seed=M + N, n_random=500)
+        assert_exact(C[rows, cols], oracle.gemm_entries(A, B, rows, cols).c32,
+                     f"{M}x{N}x{K} (direct)")
 
 
 @pytest.mark.parametrize("variant", [tra.AUTO, tra.MFMA, tra.MFMA_STREAMK],
